@@ -1,0 +1,916 @@
+// Host side of the C ABI: argument validation, per-head buffer layout and ring
+// bookkeeping (HeadCast Sec. 4.3), the work planner of the routed step (Sec. 4.4),
+// the classifier's host reductions (Sec. 4.2 Eqs. 3-5) and kernel launches.
+#include "../../include/headcast.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <functional>
+#include <mutex>
+#include <queue>
+#include <string>
+#include <vector>
+
+#include "hc_internal.h"
+
+using namespace hc;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hc_status fail(hc_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+hc_status ok() {
+  g_last_error.clear();
+  return HC_OK;
+}
+
+#define HC_TRY(expr)                       \
+  do {                                     \
+    hc_status _st = (expr);                \
+    if (_st != HC_OK) return _st;          \
+  } while (0)
+
+#define HC_HIP(expr)                                                                  \
+  do {                                                                                \
+    hipError_t _e = (expr);                                                           \
+    if (_e != hipSuccess) return fail(HC_ERR_HIP, "%s: %s", #expr, hipGetErrorString(_e)); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+size_t esize(const hc_layer_desc& d) { return d.dtype == HC_BF16 ? 2 : 4; }
+int64_t tokens_per_frame(const hc_layer_desc& d) { return (int64_t)d.frame_h * d.frame_w; }
+int64_t lq_of(const hc_layer_desc& d) { return (int64_t)d.chunk_frames * tokens_per_frame(d); }
+int rolling_blocks(const hc_layer_desc& d) { return std::max(d.window_frames / d.chunk_frames - 2, 0); }
+
+hc_status check_desc(const hc_layer_desc* d) {
+  if (!d) return fail(HC_ERR_NULL, "desc is NULL");
+  if (d->dtype != HC_BF16 && d->dtype != HC_F32) return fail(HC_ERR_DTYPE, "dtype %d unknown", d->dtype);
+  if (d->num_heads < 1 || d->num_heads > kMaxEntries)
+    return fail(HC_ERR_SHAPE, "num_heads %d outside 1..%d", d->num_heads, kMaxEntries);
+  if (d->head_dim != 64 && d->head_dim != 128) return fail(HC_ERR_SHAPE, "head_dim %d not 64 or 128", d->head_dim);
+  if (d->frame_h < 1 || d->frame_w < 1 || d->frame_h > 32767 || d->frame_w > 32767)
+    return fail(HC_ERR_SHAPE, "frame %dx%d out of range", d->frame_h, d->frame_w);
+  if (d->chunk_frames < 1 || d->window_frames < d->chunk_frames || d->window_frames % d->chunk_frames)
+    return fail(HC_ERR_SHAPE, "window_frames %d must be a positive multiple of chunk_frames %d",
+                d->window_frames, d->chunk_frames);
+  if (d->grid_h < 1 || d->grid_w < 1) return fail(HC_ERR_SHAPE, "grid %dx%d must be >= 1", d->grid_h, d->grid_w);
+  if (!(d->softmax_scale > 0.f) || !std::isfinite(d->softmax_scale))
+    return fail(HC_ERR_SHAPE, "softmax_scale must be positive and finite");
+  const int64_t keys = (int64_t)d->window_frames * tokens_per_frame(*d);
+  if (keys >= (int64_t(1) << 30)) return fail(HC_ERR_SHAPE, "window of %lld keys too large", (long long)keys);
+  return HC_OK;
+}
+
+hc_status check_labels(const hc_layer_desc& d, const int32_t* labels) {
+  if (!labels) return fail(HC_ERR_NULL, "labels is NULL");
+  for (int h = 0; h < d.num_heads; ++h)
+    if (labels[h] < HC_SINK || labels[h] > HC_GLOBAL)
+      return fail(HC_ERR_LABEL, "label %d of head %d outside 0..3", labels[h], h);
+  return HC_OK;
+}
+
+hc_status check_ptr(const void* p, const char* name) {
+  if (!p) return fail(HC_ERR_NULL, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) % 16) return fail(HC_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return HC_OK;
+}
+
+hc_status check_hist_frames(const hc_layer_desc& d, int32_t n) {
+  if (n < 0 || n > d.window_frames - d.chunk_frames || n % d.chunk_frames)
+    return fail(HC_ERR_SHAPE, "n_hist_frames %d must be a multiple of %d in [0, %d]", n, d.chunk_frames,
+                d.window_frames - d.chunk_frames);
+  return HC_OK;
+}
+
+// gfx950 check, once per device.
+std::mutex g_dev_mutex;
+std::vector<int> g_dev_ok;   // -1 unknown, 0 bad, 1 good
+
+hc_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(HC_ERR_DEVICE, "no HIP device");
+  std::lock_guard<std::mutex> lk(g_dev_mutex);
+  if ((int)g_dev_ok.size() <= dev) g_dev_ok.resize(dev + 1, -1);
+  if (g_dev_ok[dev] < 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(HC_ERR_DEVICE, "device %d unreadable", dev);
+    g_dev_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+  }
+  if (!g_dev_ok[dev]) return fail(HC_ERR_DEVICE, "device %d is not gfx950", dev);
+  return HC_OK;
+}
+
+// ---------------------------------------------------------------- timing
+struct TimedLaunch {
+  int kind;
+  hipEvent_t a, b;
+};
+std::mutex g_time_mutex;
+bool g_timing = false;
+std::vector<TimedLaunch> g_timed;
+
+template <class F>
+hipError_t timed(int kind, hipStream_t s, F&& launch) {
+  bool on;
+  {
+    std::lock_guard<std::mutex> lk(g_time_mutex);
+    on = g_timing;
+  }
+  if (!on) return launch();
+  hipEvent_t a, b;
+  hipError_t e = hipEventCreate(&a);
+  if (e != hipSuccess) return e;
+  if ((e = hipEventCreate(&b)) != hipSuccess) return e;
+  if ((e = hipEventRecord(a, s)) != hipSuccess) return e;
+  if ((e = launch()) != hipSuccess) return e;
+  if ((e = hipEventRecord(b, s)) != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_time_mutex);
+  g_timed.push_back({kind, a, b});
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------- dense planning
+struct Entry {
+  int64_t hist_off;
+  int32_t hist_len, cur_len, head, nsplit, split_len, slot;
+};
+
+constexpr int kSlotsPerCu = 2;    // dense workgroups resident per CU
+constexpr int kNumCu = 256;
+constexpr double kItemOverheadTiles = 3.0;
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Makespan estimate (in key tiles) of LPT list scheduling of the entries' items on
+// kNumCu * kSlotsPerCu slots; items run in order of decreasing length.
+double lpt_makespan(const std::vector<Entry>& es, int nqt) {
+  std::vector<std::pair<double, int64_t>> items;   // (cost, count)
+  for (const Entry& e : es) {
+    const int total = e.hist_len + e.cur_len;
+    for (int s = 0; s < e.nsplit; ++s) {
+      const int len = std::min(e.split_len, total - s * e.split_len);
+      const double cost = len / (double)kKeyTile + kItemOverheadTiles + (e.nsplit > 1 ? 1.0 : 0.0);
+      items.push_back({cost, nqt});
+    }
+  }
+  std::sort(items.begin(), items.end(), [](auto& a, auto& b) { return a.first > b.first; });
+  std::priority_queue<double, std::vector<double>, std::greater<double>> slots;
+  for (int i = 0; i < kNumCu * kSlotsPerCu; ++i) slots.push(0.0);
+  double makespan = 0.0;
+  for (auto& it : items)
+    for (int64_t c = 0; c < it.second; ++c) {
+      double t = slots.top() + it.first;
+      slots.pop();
+      slots.push(t);
+      makespan = std::max(makespan, t);
+    }
+  return makespan;
+}
+
+// Choose one key-split length for all entries (a multiple of the key tile): the
+// candidate with the smallest estimated makespan; splitting only when it pays.
+void plan_splits(std::vector<Entry>& es, int nqt) {
+  int max_total = 0;
+  for (const Entry& e : es) max_total = std::max(max_total, e.hist_len + e.cur_len);
+  if (max_total == 0) return;
+  double best = -1;
+  int best_len = max_total;
+  for (int k = 1; k <= 16; ++k) {
+    const int len = ceil_div(ceil_div(max_total, k), kKeyTile) * kKeyTile;
+    std::vector<Entry> trial = es;
+    for (Entry& e : trial) {
+      const int total = e.hist_len + e.cur_len;
+      e.nsplit = std::max(1, ceil_div(total, len));
+      e.split_len = ceil_div(ceil_div(total, e.nsplit), kKeyTile) * kKeyTile;
+    }
+    const double m = lpt_makespan(trial, nqt) * (1.0 + 0.01 * (k - 1));   // mild bias to fewer splits
+    if (best < 0 || m < best) {
+      best = m;
+      best_len = len;
+    }
+  }
+  for (Entry& e : es) {
+    const int total = e.hist_len + e.cur_len;
+    e.nsplit = std::max(1, ceil_div(total, best_len));
+    e.split_len = std::max(kKeyTile, ceil_div(ceil_div(std::max(total, 1), e.nsplit), kKeyTile) * kKeyTile);
+  }
+}
+
+// Launch dense entries (batched by kMaxEntries), longest items first.
+hc_status run_dense(std::vector<Entry> es, const DenseParams& base, int head_dim, int bf16, hipStream_t s,
+                    int* n_items_out = nullptr) {
+  std::stable_sort(es.begin(), es.end(), [](const Entry& a, const Entry& b) { return a.split_len > b.split_len; });
+  int total_items = 0;
+  for (size_t b0 = 0; b0 < es.size(); b0 += kMaxEntries) {
+    DenseParams p = base;
+    const size_t n = std::min(es.size() - b0, (size_t)kMaxEntries);
+    int items = 0;
+    for (size_t i = 0; i < n; ++i) {
+      const Entry& e = es[b0 + i];
+      DenseEntry& d = p.e[i];
+      d.hist_off = e.hist_off;
+      d.hist_len = e.hist_len;
+      d.cur_len = e.cur_len;
+      d.head = e.head;
+      d.nsplit = e.nsplit;
+      d.split_len = e.split_len;
+      d.slot = e.slot;
+      d.item_begin = items;
+      d.pad = 0;
+      items += e.nsplit * base.nqt;
+    }
+    p.n_entries = (int)n;
+    p.n_items = items;
+    total_items += items;
+    if (!n_items_out) {
+      HC_HIP(timed(bf16 ? K_DENSE : K_F32, s, [&] { return launch_dense(p, head_dim, bf16, s); }));
+    }
+  }
+  if (n_items_out) *n_items_out = total_items;
+  return HC_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- handle
+struct hc_head_buffers {
+  hc_layer_desc desc;
+  std::vector<int32_t> labels;
+  char* mem = nullptr;
+  size_t mem_bytes = 0;
+  size_t v_region = 0;               // byte offset of the V region (K region at 0)
+  std::vector<int64_t> head_off;     // element offset of head rows in a region, -1 = none
+  std::vector<int64_t> head_rows;    // row capacity
+  int64_t next_block = 0;
+  // routed plan (rebuilt when the ring fill changes)
+  int64_t plan_block = -1;
+  std::vector<Entry> entries;
+  std::vector<MergeEntry> merges;
+  std::vector<SpatialEntry> spatials;
+  int n_slots = 0;
+  int max_slots = 0;
+  bool plan_only = false;            // host-only handle (hc_plan_head_buffers)
+};
+
+namespace {
+
+int64_t capacity_rows(const hc_layer_desc& d, int cls) {
+  const int64_t S = tokens_per_frame(d);
+  if (d.window_frames == d.chunk_frames) return 0;
+  if (cls == HC_SINK) return (int64_t)d.chunk_frames * S;
+  if (cls == HC_DUMMY) return 0;
+  return (int64_t)(d.window_frames - d.chunk_frames) * S;
+}
+
+size_t layout(const hc_layer_desc& d, const int32_t* labels, std::vector<int64_t>* off, std::vector<int64_t>* rows) {
+  size_t bytes = 0;
+  for (int h = 0; h < d.num_heads; ++h) {
+    const int64_t r = capacity_rows(d, labels[h]);
+    if (off) off->push_back(r ? (int64_t)(bytes / esize(d)) : -1);
+    if (rows) rows->push_back(r);
+    bytes += align_up((size_t)r * d.head_dim * esize(d));
+  }
+  return bytes;   // one region (K or V)
+}
+
+// History frames currently stored for a head class, given the next block index.
+int64_t stored_frames(const hc_layer_desc& d, int cls, int64_t next_block) {
+  if (d.window_frames == d.chunk_frames || next_block <= 0 || cls == HC_DUMMY) return 0;
+  if (cls == HC_SINK) return d.chunk_frames;
+  const int64_t rolling = std::min<int64_t>(next_block - 1, rolling_blocks(d));
+  return (1 + rolling) * d.chunk_frames;
+}
+
+void build_plan(hc_head_buffers* b) {
+  const hc_layer_desc& d = b->desc;
+  const int64_t S = tokens_per_frame(d);
+  const int lq = (int)lq_of(d);
+  const int nqt = ceil_div(lq, kDenseQ);
+  auto make = [&](int64_t next_block) {
+    std::vector<Entry> es;
+    for (int h = 0; h < d.num_heads; ++h) {
+      const int cls = b->labels[h];
+      Entry e{};
+      e.head = h;
+      e.cur_len = lq;
+      e.slot = -1;
+      e.hist_off = b->head_off[h] < 0 ? 0 : b->head_off[h];
+      if (cls == HC_SINK || cls == HC_GLOBAL) e.hist_len = (int)(stored_frames(d, cls, next_block) * S);
+      es.push_back(e);
+    }
+    plan_splits(es, nqt);
+    return es;
+  };
+  std::vector<Entry> es = make(b->next_block);
+  // slots: split heads and Spatial heads write fp32 partials
+  int slot = 0;
+  b->merges.clear();
+  b->spatials.clear();
+  for (Entry& e : es) {
+    const int cls = b->labels[e.head];
+    if (cls == HC_SPATIAL) {
+      e.nsplit = 1;
+      e.split_len = ceil_div(e.cur_len, kKeyTile) * kKeyTile;
+      e.slot = slot++;
+      SpatialEntry se{};
+      se.hist_off = b->head_off[e.head] < 0 ? 0 : b->head_off[e.head];
+      se.head = e.head;
+      se.cur_slot = e.slot;
+      se.out_slot = -1;
+      b->spatials.push_back(se);
+    } else if (e.nsplit > 1) {
+      e.slot = slot;
+      b->merges.push_back(MergeEntry{e.head, slot, e.nsplit, 0});
+      slot += e.nsplit;
+    }
+  }
+  b->entries = es;
+  b->n_slots = slot;
+  b->plan_block = b->next_block;
+  // workspace sized for the full ring (the most slots any fill state needs)
+  std::vector<Entry> full = make(1 + rolling_blocks(d));
+  int ms = 0;
+  for (const Entry& e : full) {
+    const int cls = b->labels[e.head];
+    ms += cls == HC_SPATIAL ? 1 : (e.nsplit > 1 ? e.nsplit : 0);
+  }
+  b->max_slots = std::max(ms, slot);
+}
+
+size_t partial_bytes(int slots, int64_t lq, int head_dim) {
+  return align_up((size_t)slots * lq * head_dim * 4) + align_up((size_t)slots * lq * 2 * 4);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- ABI
+extern "C" {
+
+const char* hc_status_string(int st) {
+  switch (st) {
+    case HC_OK: return "ok";
+    case HC_ERR_NULL: return "null pointer";
+    case HC_ERR_SHAPE: return "bad shape";
+    case HC_ERR_DTYPE: return "bad dtype";
+    case HC_ERR_LABEL: return "bad label";
+    case HC_ERR_WORKSPACE: return "workspace too small";
+    case HC_ERR_ALIGN: return "misaligned pointer";
+    case HC_ERR_DEVICE: return "no gfx950 device";
+    case HC_ERR_HIP: return "HIP error";
+    case HC_ERR_STATE: return "bad state";
+    default: return "unknown status";
+  }
+}
+
+const char* hc_last_error(void) { return g_last_error.c_str(); }
+
+hc_status hc_default_classify_params(hc_classify_params* p) {
+  if (!p) return fail(HC_ERR_NULL, "params is NULL");
+  p->theta_sink = p->theta_dummy = p->theta_spatial = 0.95f;
+  p->theta_score = 0.755f;
+  p->gamma = 5.0f;
+  p->percentile = 5.0f;
+  p->proxy_grid_h = p->proxy_grid_w = 0;
+  p->sink_proxy_includes_current = 0;
+  return ok();
+}
+
+hc_status hc_head_buffers_bytes(const hc_layer_desc* desc, const int32_t* labels, size_t* bytes) {
+  HC_TRY(check_desc(desc));
+  HC_TRY(check_labels(*desc, labels));
+  if (!bytes) return fail(HC_ERR_NULL, "bytes is NULL");
+  *bytes = 2 * layout(*desc, labels, nullptr, nullptr);
+  return ok();
+}
+
+hc_status hc_build_head_buffers(const hc_layer_desc* desc, const int32_t* labels, const void* k_hist,
+                                const void* v_hist, int32_t n_hist_frames, void* buffer_mem,
+                                size_t buffer_bytes, hc_head_buffers** out, void* stream) {
+  HC_TRY(check_desc(desc));
+  HC_TRY(check_labels(*desc, labels));
+  HC_TRY(check_hist_frames(*desc, n_hist_frames));
+  if (!out) return fail(HC_ERR_NULL, "out is NULL");
+  const size_t need = 2 * layout(*desc, labels, nullptr, nullptr);
+  if (need > 0) HC_TRY(check_ptr(buffer_mem, "buffer_mem"));
+  if (buffer_bytes < need) return fail(HC_ERR_WORKSPACE, "buffer_mem has %zu bytes, needs %zu", buffer_bytes, need);
+  if (n_hist_frames > 0) {
+    HC_TRY(check_ptr(k_hist, "k_hist"));
+    HC_TRY(check_ptr(v_hist, "v_hist"));
+  }
+  HC_TRY(check_device());
+
+  hc_head_buffers* b = new hc_head_buffers();
+  b->desc = *desc;
+  b->labels.assign(labels, labels + desc->num_heads);
+  b->mem = (char*)buffer_mem;
+  b->mem_bytes = buffer_bytes;
+  b->v_region = layout(*desc, labels, &b->head_off, &b->head_rows);
+  b->next_block = n_hist_frames / desc->chunk_frames;
+
+  const hc_layer_desc& d = *desc;
+  const int64_t S = tokens_per_frame(d);
+  const size_t es_ = esize(d);
+  hipStream_t s = (hipStream_t)stream;
+  // Build: the stored frames are a prefix of the logical history (block b <= R sits at
+  // position b), so each head copies one contiguous row range.
+  for (int pass = 0; pass < 2 && n_hist_frames > 0; ++pass) {
+    CopyParams p{};
+    p.src_k = k_hist;
+    p.src_v = v_hist;
+    p.dst_k = b->mem;
+    p.dst_v = b->mem + b->v_region;
+    p.src_stride = (int64_t)d.num_heads * d.head_dim * es_;
+    p.row_bytes = d.head_dim * (int)es_;
+    int n = 0;
+    for (int h = 0; h < d.num_heads; ++h) {
+      const int cls = b->labels[h];
+      if (b->head_off[h] < 0 || (pass == 0) != (cls == HC_SINK)) continue;
+      p.e[n].src_off = (int64_t)h * d.head_dim * es_;
+      p.e[n].dst_off = b->head_off[h] * (int64_t)es_;
+      ++n;
+    }
+    p.n_entries = n;
+    p.rows = (int)(stored_frames(d, pass == 0 ? HC_SINK : HC_GLOBAL, b->next_block) * S);
+    if (n) {
+      hipError_t e = timed(K_COPY, s, [&] { return launch_copy(p, s); });
+      if (e != hipSuccess) {
+        delete b;
+        return fail(HC_ERR_HIP, "build copy: %s", hipGetErrorString(e));
+      }
+    }
+  }
+  build_plan(b);
+  *out = b;
+  return ok();
+}
+
+hc_status hc_plan_head_buffers(const hc_layer_desc* desc, const int32_t* labels, int64_t next_block,
+                               hc_head_buffers** out) {
+  HC_TRY(check_desc(desc));
+  HC_TRY(check_labels(*desc, labels));
+  if (!out) return fail(HC_ERR_NULL, "out is NULL");
+  if (next_block < 0) return fail(HC_ERR_SHAPE, "next_block %lld negative", (long long)next_block);
+  hc_head_buffers* b = new hc_head_buffers();
+  b->desc = *desc;
+  b->labels.assign(labels, labels + desc->num_heads);
+  b->v_region = layout(*desc, labels, &b->head_off, &b->head_rows);
+  b->next_block = next_block;
+  b->plan_only = true;
+  build_plan(b);
+  *out = b;
+  return ok();
+}
+
+hc_status hc_append_chunk(hc_head_buffers* b, const void* k_chunk, const void* v_chunk, void* stream) {
+  if (!b) return fail(HC_ERR_NULL, "buffers is NULL");
+  if (b->plan_only) return fail(HC_ERR_STATE, "a planning handle holds no device buffers");
+  HC_TRY(check_ptr(k_chunk, "k_chunk"));
+  HC_TRY(check_ptr(v_chunk, "v_chunk"));
+  HC_TRY(check_device());
+  const hc_layer_desc& d = b->desc;
+  const int64_t blk = b->next_block;
+  const int R = rolling_blocks(d);
+  int pos = -1;   // block position inside the buffers
+  if (d.window_frames > d.chunk_frames) pos = blk == 0 ? 0 : (R > 0 ? 1 + (int)((blk - 1) % R) : -1);
+  if (pos >= 0) {
+    const int64_t S = tokens_per_frame(d);
+    const size_t es_ = esize(d);
+    CopyParams p{};
+    p.src_k = k_chunk;
+    p.src_v = v_chunk;
+    p.dst_k = b->mem;
+    p.dst_v = b->mem + b->v_region;
+    p.src_stride = (int64_t)d.num_heads * d.head_dim * es_;
+    p.row_bytes = d.head_dim * (int)es_;
+    p.rows = (int)(d.chunk_frames * S);
+    int n = 0;
+    for (int h = 0; h < d.num_heads; ++h) {
+      const int cls = b->labels[h];
+      if (b->head_off[h] < 0) continue;
+      if (cls == HC_SINK && pos != 0) continue;
+      p.e[n].src_off = (int64_t)h * d.head_dim * es_;
+      p.e[n].dst_off = (b->head_off[h] + (int64_t)pos * d.chunk_frames * S * d.head_dim) * (int64_t)es_;
+      ++n;
+    }
+    p.n_entries = n;
+    HC_HIP(timed(K_COPY, (hipStream_t)stream, [&] { return launch_copy(p, (hipStream_t)stream); }));
+  }
+  b->next_block = blk + 1;
+  build_plan(b);
+  return ok();
+}
+
+hc_status hc_buffers_state(const hc_head_buffers* b, int64_t* next_block) {
+  if (!b || !next_block) return fail(HC_ERR_NULL, "NULL argument");
+  *next_block = b->next_block;
+  return ok();
+}
+
+hc_status hc_free_head_buffers(hc_head_buffers* b) {
+  delete b;
+  return ok();
+}
+
+hc_status hc_routed_workspace_bytes(const hc_head_buffers* b, size_t* bytes) {
+  if (!b || !bytes) return fail(HC_ERR_NULL, "NULL argument");
+  *bytes = partial_bytes(b->max_slots, lq_of(b->desc), b->desc.head_dim);
+  return ok();
+}
+
+hc_status hc_routed_attention(const hc_head_buffers* b, const void* q, const void* k_cur, const void* v_cur,
+                              void* out, void* workspace, size_t ws_bytes, void* stream) {
+  if (!b) return fail(HC_ERR_NULL, "buffers is NULL");
+  if (b->plan_only) return fail(HC_ERR_STATE, "a planning handle holds no device buffers");
+  HC_TRY(check_ptr(q, "q"));
+  HC_TRY(check_ptr(k_cur, "k_cur"));
+  HC_TRY(check_ptr(v_cur, "v_cur"));
+  HC_TRY(check_ptr(out, "out"));
+  const hc_layer_desc& d = b->desc;
+  const int64_t lq = lq_of(d);
+  const size_t need = partial_bytes(b->n_slots, lq, d.head_dim);
+  if (b->n_slots > 0) HC_TRY(check_ptr(workspace, "workspace"));
+  if (ws_bytes < need) return fail(HC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  HC_TRY(check_device());
+  hipStream_t s = (hipStream_t)stream;
+  const int bf16 = d.dtype == HC_BF16;
+  float* part_o = (float*)workspace;
+  float* part_ml = (float*)((char*)workspace + align_up((size_t)b->n_slots * lq * d.head_dim * 4));
+
+  DenseParams p{};
+  p.q = q;
+  p.k_hist = b->mem;
+  p.v_hist = b->mem + b->v_region;
+  p.k_cur = k_cur;
+  p.v_cur = v_cur;
+  p.out = out;
+  p.part_o = part_o;
+  p.part_ml = part_ml;
+  p.hist_stride = d.head_dim;
+  p.tok_stride = (int64_t)d.num_heads * d.head_dim;
+  p.lq = (int)lq;
+  p.nqt = ceil_div(lq, kDenseQ);
+  p.scale_log2 = d.softmax_scale * 1.4426950408889634f;
+  HC_TRY(run_dense(b->entries, p, d.head_dim, bf16, s));
+
+  if (!b->merges.empty()) {
+    MergeParams m{};
+    m.part_o = part_o;
+    m.part_ml = part_ml;
+    m.out = out;
+    m.tok_stride = p.tok_stride;
+    m.lq = (int)lq;
+    m.head_dim = d.head_dim;
+    m.n_entries = (int)b->merges.size();
+    for (size_t i = 0; i < b->merges.size(); ++i) m.e[i] = b->merges[i];
+    HC_HIP(timed(K_MERGE, s, [&] { return launch_merge(m, d.head_dim, bf16, s); }));
+  }
+  if (!b->spatials.empty()) {
+    SpatialParams sp{};
+    sp.q = q;
+    sp.k_hist = b->mem;
+    sp.v_hist = b->mem + b->v_region;
+    sp.out = out;
+    sp.part_o = part_o;
+    sp.part_ml = part_ml;
+    sp.hist_stride = d.head_dim;
+    sp.tok_stride = p.tok_stride;
+    sp.lq = (int)lq;
+    sp.frame_h = d.frame_h;
+    sp.frame_w = d.frame_w;
+    sp.chunk_frames = d.chunk_frames;
+    sp.n_hist_frames = (int)stored_frames(d, HC_SPATIAL, b->next_block);
+    sp.grid_h = d.grid_h;
+    sp.grid_w = d.grid_w;
+    sp.tiles_r = ceil_div(d.frame_h, kSpTileR);
+    sp.tiles_c = ceil_div(d.frame_w, kSpTileC);
+    sp.scale_log2 = p.scale_log2;
+    sp.n_entries = (int)b->spatials.size();
+    for (size_t i = 0; i < b->spatials.size(); ++i) sp.e[i] = b->spatials[i];
+    HC_HIP(timed(bf16 ? K_SPATIAL : K_F32, s, [&] { return launch_spatial(sp, d.head_dim, bf16, s); }));
+  }
+  return ok();
+}
+
+// ---------------------------------------------------------------- classification
+namespace {
+
+struct ClassifyLayout {
+  int n_mid, slots_per_head, slots;
+  size_t part_o, part_ml, stats, total;
+};
+
+ClassifyLayout classify_layout(const hc_layer_desc& d, int32_t n_hist) {
+  ClassifyLayout L{};
+  const int64_t lq = lq_of(d);
+  // middle history frames, split into ranges of one block (rounded up to the key tile)
+  const int64_t blk = (int64_t)d.chunk_frames * tokens_per_frame(d);
+  const int64_t split = (blk + kKeyTile - 1) / kKeyTile * kKeyTile;
+  const int64_t mid_keys = (int64_t)std::max(0, n_hist - d.chunk_frames) * tokens_per_frame(d);
+  L.n_mid = (int)((mid_keys + split - 1) / split);
+  L.slots_per_head = 3 + L.n_mid;
+  L.slots = L.slots_per_head * d.num_heads;
+  L.part_o = 0;
+  L.part_ml = align_up((size_t)L.slots * lq * d.head_dim * 4);
+  L.stats = L.part_ml + align_up((size_t)L.slots * lq * 2 * 4);
+  L.total = L.stats + align_up((size_t)d.num_heads * lq * 4 * 4);
+  return L;
+}
+
+hc_status check_params(const hc_classify_params* p) {
+  if (!p) return fail(HC_ERR_NULL, "params is NULL");
+  if (!(p->percentile >= 0.f && p->percentile <= 100.f)) return fail(HC_ERR_SHAPE, "percentile outside [0, 100]");
+  if (p->proxy_grid_h < 0 || p->proxy_grid_w < 0) return fail(HC_ERR_SHAPE, "negative proxy grid");
+  return HC_OK;
+}
+
+}  // namespace
+
+hc_status hc_classify_workspace_bytes(const hc_layer_desc* desc, const hc_classify_params* params,
+                                      int32_t n_hist_frames, size_t* bytes) {
+  HC_TRY(check_desc(desc));
+  HC_TRY(check_params(params));
+  HC_TRY(check_hist_frames(*desc, n_hist_frames));
+  if (!bytes) return fail(HC_ERR_NULL, "bytes is NULL");
+  *bytes = classify_layout(*desc, n_hist_frames).total;
+  return ok();
+}
+
+hc_status hc_reduce_statistics(const float* per_token, int64_t lq, int32_t head_dim, double gamma,
+                               double percentile, double* out) {
+  if (!per_token || !out) return fail(HC_ERR_NULL, "NULL argument");
+  if (lq < 1 || head_dim < 1) return fail(HC_ERR_SHAPE, "empty statistics");
+  double s0 = 0, s1 = 0, s2 = 0, se = 0;
+  std::vector<double> cp(lq);
+  for (int64_t t = 0; t < lq; ++t) {
+    s0 += per_token[t * 4 + 0];
+    s1 += per_token[t * 4 + 1];
+    s2 += per_token[t * 4 + 2];
+    se += per_token[t * 4 + 3];
+    cp[t] = per_token[t * 4 + 2];
+  }
+  std::sort(cp.begin(), cp.end());
+  const double pos = percentile / 100.0 * (double)(lq - 1);
+  const int64_t i = std::min<int64_t>((int64_t)std::floor(pos), lq - 1);
+  const double frac = pos - (double)i;
+  const double pct = i + 1 < lq ? cp[i] + frac * (cp[i + 1] - cp[i]) : cp[i];
+  const double mse = se / ((double)lq * head_dim);
+  out[0] = s0 / lq;
+  out[1] = s1 / lq;
+  out[2] = s2 / lq;
+  out[3] = pct;
+  out[4] = mse;
+  out[5] = pct - gamma * mse;
+  return ok();
+}
+
+int32_t hc_decide(double cs, double cd, double cp, double score, const hc_classify_params* p) {
+  hc_classify_params def;
+  if (!p) {
+    hc_default_classify_params(&def);
+    p = &def;
+  }
+  if (cs >= (double)p->theta_sink) return HC_SINK;
+  if (cd >= (double)p->theta_dummy) return HC_DUMMY;
+  if (cp >= (double)p->theta_spatial && score >= (double)p->theta_score) return HC_SPATIAL;
+  return HC_GLOBAL;
+}
+
+hc_status hc_classify_heads(const hc_layer_desc* desc, const hc_classify_params* params, const void* q,
+                            const void* k_hist, const void* v_hist, int32_t n_hist_frames, const void* k_cur,
+                            const void* v_cur, void* workspace, size_t ws_bytes, int32_t* labels_out,
+                            double* stats_out, void* stream) {
+  HC_TRY(check_desc(desc));
+  HC_TRY(check_params(params));
+  HC_TRY(check_hist_frames(*desc, n_hist_frames));
+  const hc_layer_desc& d = *desc;
+  if (n_hist_frames < d.chunk_frames)
+    return fail(HC_ERR_STATE, "classification needs the sink block: n_hist_frames %d < %d", n_hist_frames,
+                d.chunk_frames);
+  HC_TRY(check_ptr(q, "q"));
+  HC_TRY(check_ptr(k_hist, "k_hist"));
+  HC_TRY(check_ptr(v_hist, "v_hist"));
+  HC_TRY(check_ptr(k_cur, "k_cur"));
+  HC_TRY(check_ptr(v_cur, "v_cur"));
+  HC_TRY(check_ptr(workspace, "workspace"));
+  if (!labels_out) return fail(HC_ERR_NULL, "labels_out is NULL");
+  const ClassifyLayout L = classify_layout(d, n_hist_frames);
+  if (ws_bytes < L.total) return fail(HC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+  HC_TRY(check_device());
+
+  hipStream_t s = (hipStream_t)stream;
+  const int bf16 = d.dtype == HC_BF16;
+  const int64_t S = tokens_per_frame(d);
+  const int64_t lq = lq_of(d);
+  const int H = d.num_heads, D = d.head_dim;
+  float* part_o = (float*)((char*)workspace + L.part_o);
+  float* part_ml = (float*)((char*)workspace + L.part_ml);
+  float* stats = (float*)((char*)workspace + L.stats);
+
+  // Dense partials per head: current block (slot 0), sink block (slot 1), and one
+  // slot per middle block (slots 3..): each is one C*S-key range.
+  std::vector<Entry> es;
+  const int blk = (int)(d.chunk_frames * S);
+  for (int h = 0; h < H; ++h) {
+    const int base = h * L.slots_per_head;
+    Entry cur{0, 0, blk, h, 1, blk, base};
+    cur.split_len = ceil_div(blk, kKeyTile) * kKeyTile;
+    Entry first{(int64_t)h * D, blk, 0, h, 1, cur.split_len, base + 1};
+    es.push_back(cur);
+    es.push_back(first);
+    if (L.n_mid > 0) {
+      Entry mid{(int64_t)h * D + (int64_t)blk * H * D, L.n_mid * blk, 0, h, L.n_mid, cur.split_len, base + 3};
+      es.push_back(mid);
+    }
+  }
+  DenseParams p{};
+  p.q = q;
+  p.k_hist = k_hist;
+  p.v_hist = v_hist;
+  p.k_cur = k_cur;
+  p.v_cur = v_cur;
+  p.out = nullptr;
+  p.part_o = part_o;
+  p.part_ml = part_ml;
+  p.hist_stride = (int64_t)H * D;
+  p.tok_stride = (int64_t)H * D;
+  p.lq = (int)lq;
+  p.nqt = ceil_div(lq, kDenseQ);
+  p.scale_log2 = d.softmax_scale * 1.4426950408889634f;
+  HC_TRY(run_dense(es, p, D, bf16, s));
+
+  // Spatial proxy: gathered history windows of every head (slot 2), partial mode.
+  SpatialParams sp{};
+  sp.q = q;
+  sp.k_hist = k_hist;
+  sp.v_hist = v_hist;
+  sp.part_o = part_o;
+  sp.part_ml = part_ml;
+  sp.hist_stride = (int64_t)H * D;
+  sp.tok_stride = (int64_t)H * D;
+  sp.lq = (int)lq;
+  sp.frame_h = d.frame_h;
+  sp.frame_w = d.frame_w;
+  sp.chunk_frames = d.chunk_frames;
+  sp.n_hist_frames = n_hist_frames;
+  sp.grid_h = params->proxy_grid_h > 0 ? params->proxy_grid_h : d.grid_h;
+  sp.grid_w = params->proxy_grid_w > 0 ? params->proxy_grid_w : d.grid_w;
+  sp.tiles_r = ceil_div(d.frame_h, kSpTileR);
+  sp.tiles_c = ceil_div(d.frame_w, kSpTileC);
+  sp.scale_log2 = p.scale_log2;
+  for (int h0 = 0; h0 < H; h0 += kMaxEntries) {
+    const int n = std::min(H - h0, kMaxEntries);
+    for (int i = 0; i < n; ++i) {
+      const int h = h0 + i;
+      sp.e[i] = SpatialEntry{(int64_t)h * D, h, -1, h * L.slots_per_head + 2, 0};
+    }
+    sp.n_entries = n;
+    HC_HIP(timed(bf16 ? K_SPATIAL : K_F32, s, [&] { return launch_spatial(sp, D, bf16, s); }));
+  }
+
+  StatsParams st{};
+  st.part_o = part_o;
+  st.part_ml = part_ml;
+  st.stats = stats;
+  st.lq = (int)lq;
+  st.num_heads = H;
+  st.head_dim = D;
+  st.n_mid = L.n_mid;
+  st.sink_with_cur = params->sink_proxy_includes_current ? 1 : 0;
+  st.slots_per_head = L.slots_per_head;
+  HC_HIP(timed(K_STATS, s, [&] { return launch_stats(st, s); }));
+
+  std::vector<float> host((size_t)H * lq * 4);
+  HC_HIP(hipMemcpyAsync(host.data(), stats, host.size() * sizeof(float), hipMemcpyDeviceToHost, s));
+  HC_HIP(hipStreamSynchronize(s));
+  for (int h = 0; h < H; ++h) {
+    double out6[6];
+    HC_TRY(hc_reduce_statistics(host.data() + (size_t)h * lq * 4, lq, D, params->gamma, params->percentile, out6));
+    labels_out[h] = hc_decide(out6[0], out6[1], out6[2], out6[5], params);
+    if (stats_out)
+      for (int i = 0; i < 6; ++i) stats_out[h * 6 + i] = out6[i];
+  }
+  return ok();
+}
+
+// ---------------------------------------------------------------- index exports
+hc_status hc_debug_slot_table(const hc_head_buffers* b, int32_t* frames) {
+  if (!b || !frames) return fail(HC_ERR_NULL, "NULL argument");
+  const hc_layer_desc& d = b->desc;
+  const int C = d.chunk_frames, HF = d.window_frames - C;
+  const int R = rolling_blocks(d);
+  for (int h = 0; h < d.num_heads; ++h) {
+    int32_t* row = frames + (size_t)h * HF;
+    for (int i = 0; i < HF; ++i) row[i] = -1;
+    const int cls = b->labels[h];
+    if (cls == HC_DUMMY || HF == 0 || b->next_block <= 0) continue;
+    for (int i = 0; i < C; ++i) row[i] = i;   // sink block (absolute block 0)
+    if (cls == HC_SINK || R == 0) continue;
+    // the latest block stored at each rolling position
+    for (int64_t blk = std::max<int64_t>(1, b->next_block - R); blk < b->next_block; ++blk) {
+      const int pos = 1 + (int)((blk - 1) % R);
+      for (int i = 0; i < C; ++i) row[pos * C + i] = (int32_t)(blk * C + i);
+    }
+  }
+  return ok();
+}
+
+hc_status hc_debug_head_region(const hc_head_buffers* b, int32_t head, int64_t* k_offset, int64_t* v_offset,
+                               int64_t* rows) {
+  if (!b || !k_offset || !v_offset || !rows) return fail(HC_ERR_NULL, "NULL argument");
+  if (head < 0 || head >= b->desc.num_heads) return fail(HC_ERR_SHAPE, "head %d out of range", head);
+  const size_t es_ = esize(b->desc);
+  if (b->head_off[head] < 0) {
+    *k_offset = *v_offset = -1;
+    *rows = 0;
+  } else {
+    *k_offset = b->head_off[head] * (int64_t)es_;
+    *v_offset = (int64_t)b->v_region + b->head_off[head] * (int64_t)es_;
+    *rows = b->head_rows[head];
+  }
+  return ok();
+}
+
+hc_status hc_debug_gather_origins(const hc_layer_desc* desc, int32_t grid_h, int32_t grid_w, void* r0c0,
+                                  void* stream) {
+  HC_TRY(check_desc(desc));
+  HC_TRY(check_ptr(r0c0, "r0c0"));
+  if (grid_h < 1 || grid_w < 1) return fail(HC_ERR_SHAPE, "grid must be >= 1");
+  HC_TRY(check_device());
+  HC_HIP(launch_gather_origins(desc->frame_h, desc->frame_w, grid_h, grid_w, (int32_t*)r0c0, (hipStream_t)stream));
+  return ok();
+}
+
+hc_status hc_debug_routed_plan(const hc_head_buffers* b, int32_t* entries, int32_t max_entries, int32_t* n_entries,
+                               int32_t* n_items) {
+  if (!b || !n_entries || !n_items) return fail(HC_ERR_NULL, "NULL argument");
+  std::vector<Entry> es = b->entries;
+  std::stable_sort(es.begin(), es.end(), [](const Entry& a, const Entry& x) { return a.split_len > x.split_len; });
+  const int nqt = ceil_div(lq_of(b->desc), kDenseQ);
+  int items = 0;
+  for (size_t i = 0; i < es.size(); ++i) {
+    if (entries && (int)i < max_entries) {
+      int32_t* r = entries + i * 8;
+      r[0] = es[i].head;
+      r[1] = es[i].hist_len;
+      r[2] = es[i].cur_len;
+      r[3] = es[i].nsplit;
+      r[4] = es[i].split_len;
+      r[5] = es[i].slot;
+      r[6] = items;
+      r[7] = 0;
+    }
+    items += es[i].nsplit * nqt;
+  }
+  *n_entries = (int32_t)es.size();
+  *n_items = items;
+  return ok();
+}
+
+hc_status hc_timing_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_time_mutex);
+  g_timing = enable != 0;
+  return ok();
+}
+
+hc_status hc_timing_read(double* ms_out, int64_t* counts_out) {
+  if (!ms_out || !counts_out) return fail(HC_ERR_NULL, "NULL argument");
+  std::vector<TimedLaunch> v;
+  {
+    std::lock_guard<std::mutex> lk(g_time_mutex);
+    v.swap(g_timed);
+  }
+  for (int i = 0; i < K_NUM; ++i) {
+    ms_out[i] = 0.0;
+    counts_out[i] = 0;
+  }
+  hc_status st = HC_OK;
+  for (auto& t : v) {
+    float ms = 0.f;
+    if (hipEventSynchronize(t.b) != hipSuccess || hipEventElapsedTime(&ms, t.a, t.b) != hipSuccess)
+      st = fail(HC_ERR_HIP, "event timing failed");
+    ms_out[t.kind] += ms;
+    counts_out[t.kind] += 1;
+    (void)hipEventDestroy(t.a);
+    (void)hipEventDestroy(t.b);
+  }
+  return st == HC_OK ? ok() : st;
+}
+
+}  // extern "C"

@@ -1,0 +1,154 @@
+// Internal structures shared by the host planner (hc_api.cpp) and the HIP kernels.
+// Not part of the public ABI (include/headcast.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hc {
+
+constexpr int kMaxEntries = 64;   // dense work entries per launch (kernel arguments by value)
+constexpr int kKeyTile = 64;      // keys per LDS tile in the dense and spatial kernels
+constexpr int kDenseWaves = 4;    // waves per dense workgroup
+constexpr int kDenseQ = 32 * kDenseWaves;   // queries per dense workgroup
+constexpr int kXcdGroup = 8;      // consecutive items (same key range) kept on one XCD
+constexpr int kSpTileR = 4;       // Spatial query tile: 4 rows x 8 cols of positions
+constexpr int kSpTileC = 8;
+
+// One dense work entry: a head's queries against one contiguous key range made of
+// [history rows 0..hist_len) followed by [current-block rows 0..cur_len). The range is
+// split into nsplit pieces of split_len keys; every (split, query tile) is one item.
+struct DenseEntry {
+  int64_t hist_off;    // element offset of history row 0 (into k_hist / v_hist)
+  int32_t hist_len;    // history keys
+  int32_t cur_len;     // current-block keys (0 or C*S)
+  int32_t head;        // head index: column of q / k_cur / v_cur / out
+  int32_t nsplit;      // key splits
+  int32_t split_len;   // keys per split (multiple of kKeyTile)
+  int32_t slot;        // first partial slot, or -1: write the normalised output
+  int32_t item_begin;  // index of this entry's first item
+  int32_t pad;
+};
+
+struct DenseParams {
+  const void* q;         // [lq][H][D]
+  const void* k_hist;    // history rows, row stride hist_stride elements
+  const void* v_hist;
+  const void* k_cur;     // [C*S][H][D]
+  const void* v_cur;
+  void* out;             // [lq][H][D], same dtype as q
+  float* part_o;         // [slot][lq][D] fp32, unnormalised
+  float* part_ml;        // [slot][lq][2]: running max (log2 units, scale folded) and sum
+  int64_t hist_stride;   // elements between consecutive history rows
+  int64_t tok_stride;    // H*D: elements between tokens of q / k_cur / v_cur / out
+  int32_t lq;            // queries per head
+  int32_t nqt;           // query tiles per head
+  int32_t n_entries;
+  int32_t n_items;
+  float scale_log2;      // softmax_scale * log2(e)
+  int32_t pad;
+  DenseEntry e[kMaxEntries];
+};
+
+// Merge of partial slots into the normalised output (split keys, Spatial merge).
+struct MergeEntry {
+  int32_t head;
+  int32_t slot;
+  int32_t nslot;
+  int32_t pad;
+};
+
+struct MergeParams {
+  const float* part_o;
+  const float* part_ml;
+  void* out;
+  int64_t tok_stride;
+  int32_t lq;
+  int32_t n_entries;
+  int32_t head_dim;
+  int32_t pad;
+  MergeEntry e[kMaxEntries];
+};
+
+// Spatial history gather for the Spatial heads: every query (f, r, c) of the current
+// block against the g x g window of every history frame; merged with the dense
+// current-block partial held in cur_slot (final mode), or written as a partial.
+struct SpatialEntry {
+  int64_t hist_off;   // element offset of history row 0
+  int32_t head;
+  int32_t cur_slot;   // partial slot of the current-block part; -1 in partial mode
+  int32_t out_slot;   // partial slot to write (partial mode), -1 in final mode
+  int32_t pad;
+};
+
+struct SpatialParams {
+  const void* q;
+  const void* k_hist;
+  const void* v_hist;
+  void* out;
+  float* part_o;
+  float* part_ml;
+  int64_t hist_stride;
+  int64_t tok_stride;
+  int32_t lq;
+  int32_t frame_h, frame_w, chunk_frames;
+  int32_t n_hist_frames;   // valid history frames (a prefix of the buffer positions)
+  int32_t grid_h, grid_w;
+  int32_t tiles_r, tiles_c;  // position tiles per frame
+  int32_t n_entries;
+  float scale_log2;
+  int32_t pad;
+  SpatialEntry e[kMaxEntries];
+};
+
+// Row copy: `rows` rows of row_bytes from src (byte offset src_off, byte stride
+// src_stride) to contiguous rows at dst byte offset dst_off. K and V move together.
+struct CopyEntry {
+  int64_t src_off;
+  int64_t dst_off;
+};
+
+struct CopyParams {
+  const void* src_k;
+  const void* src_v;
+  void* dst_k;
+  void* dst_v;
+  int64_t src_stride;
+  int32_t rows;
+  int32_t row_bytes;
+  int32_t n_entries;
+  int32_t pad;
+  CopyEntry e[kMaxEntries];
+};
+
+// Classifier statistics: per (head, token) cosines of the three proxies and the
+// squared error of the Spatial proxy, all against the full-window reference.
+struct StatsParams {
+  const float* part_o;
+  const float* part_ml;
+  float* stats;          // [H][lq][4]: cos_sink, cos_dummy, cos_spatial, sq_err_spatial
+  int32_t lq;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t n_mid;         // partial slots of the middle history frames per head
+  int32_t sink_with_cur; // sink proxy also sees the current block
+  int32_t pad;
+  // slot index of head h: cur = h*slots_per_head + 0, first = +1, spatial = +2, mid = +3..
+  int32_t slots_per_head;
+  int32_t pad2;
+};
+
+// Kernel ids for the optional per-kernel event timing.
+enum KernelId { K_DENSE = 0, K_MERGE, K_SPATIAL, K_COPY, K_STATS, K_F32, K_NUM };
+
+// Launchers (defined in the .hip files). Each returns the hipError_t of the launch.
+hipError_t launch_dense(const DenseParams& p, int head_dim, int bf16, hipStream_t s);
+hipError_t launch_merge(const MergeParams& p, int head_dim, int bf16, hipStream_t s);
+hipError_t launch_spatial(const SpatialParams& p, int head_dim, int bf16, hipStream_t s);
+hipError_t launch_copy(const CopyParams& p, hipStream_t s);
+hipError_t launch_stats(const StatsParams& p, hipStream_t s);
+hipError_t launch_gather_origins(int frame_h, int frame_w, int grid_h, int grid_w, int32_t* out,
+                                 hipStream_t s);
+
+int dense_items_grid(int n_items);   // workgroups launched for n_items (XCD-grouped padding)
+
+}  // namespace hc

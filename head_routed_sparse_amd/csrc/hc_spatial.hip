@@ -1,0 +1,180 @@
+// Spatial path, history part (HeadCast Sec. 3.2 "Spatial Pattern", Sec. 4.4 Spatial
+// Path, with the sliding g x g neighbourhood of the Sec. 4.2 Spatial proxy): every
+// query (f, r, c) of the current block attends, in each history frame, to the g x g
+// window whose origin is clamp(r - g/2, 0, fh - g) x clamp(c - g/2, 0, fw - g).
+//
+// A workgroup (4 waves) takes a tile of 4 x 8 positions of one Spatial head, one wave
+// per chunk frame (the chunk frames at one position share the key set exactly). For each
+// history frame it walks the union of the 32 windows in 64-key LDS tiles: K/V rows
+// are gathered as whole 256-B rows (coalesced), scores come from the same MFMA tile
+// step as the dense path, and keys outside a query's own window are masked.
+// In final mode the result is merged with the dense current-block partial by its
+// log-sum-exp and written as bf16; in partial mode (classifier) it is stored as fp32.
+#include "hc_tile.h"
+
+namespace hc {
+
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams p) {
+  using L = AttnLds<D>;
+  constexpr int KS = D / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * L::bufElems];
+  __shared__ __attribute__((aligned(16))) int kcoord[2][kKeyTile];
+
+  const SpatialEntry e = p.e[blockIdx.y];
+  const int tr = blockIdx.x / p.tiles_c, tc = blockIdx.x % p.tiles_c;
+  const int fh = p.frame_h, fw = p.frame_w, S = fh * fw;
+  const int eh = min(p.grid_h, fh), ew = min(p.grid_w, fw);
+  const int R0 = tr * kSpTileR, C0 = tc * kSpTileC;
+  const int R1 = min(R0 + kSpTileR, fh) - 1, C1 = min(C0 + kSpTileC, fw) - 1;
+  // union of the windows of the tile's positions
+  const int ur0 = win_origin(R0, p.grid_h, fh), ur1 = win_origin(R1, p.grid_h, fh) + eh;
+  const int uc0 = win_origin(C0, p.grid_w, fw), uc1 = win_origin(C1, p.grid_w, fw) + ew;
+  const int UW = uc1 - uc0;
+  const int nU = (ur1 - ur0) * UW;
+  const int nchunk = (nU + kKeyTile - 1) / kKeyTile;
+  const int n_tiles = p.n_hist_frames * nchunk;
+
+  const int tid = threadIdx.x;
+  constexpr int nwave = 4;   // one wave per chunk frame; spare waves only load
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+  const int pr = R0 + l32 / kSpTileC, pc = C0 + l32 % kSpTileC;
+  const bool pos_ok = pr < fh && pc < fw;
+  const int r0q = win_origin(min(pr, fh - 1), p.grid_h, fh);
+  const int c0q = win_origin(min(pc, fw - 1), p.grid_w, fw);
+
+  const uint16_t* kh = (const uint16_t*)p.k_hist + e.hist_off;
+  const uint16_t* vh = (const uint16_t*)p.v_hist + e.hist_off;
+  const int64_t hs = p.hist_stride;
+
+  TileRegs<D> regs;
+  auto key_row = [&](int t, int j) -> int64_t {   // history row of local key j of tile t
+    const int f = t / nchunk;
+    const int ui = min((t - f * nchunk) * kKeyTile + j, nU - 1);
+    const int kr = ur0 + ui / UW, kcol = uc0 + ui % UW;
+    return (int64_t)f * S + (int64_t)kr * fw + kcol;
+  };
+  auto load = [&](int t) {
+    load_tile<D>(regs, [&](int j) { return kh + key_row(t, j) * hs; },
+                 [&](int j) { return vh + key_row(t, j) * hs; }, tid);
+  };
+  auto store = [&](int t, int b) {
+    if (tid < kKeyTile) {
+      const int f = t / nchunk;
+      const int ui = (t - f * nchunk) * kKeyTile + tid;
+      kcoord[b][tid] = ui < nU ? (((ur0 + ui / UW) << 16) | (uc0 + ui % UW)) : 0x7FFF0000;
+    }
+    store_tile<D>(regs, lds + b * L::bufElems, tid);
+  };
+
+  for (int cf0 = 0; cf0 < p.chunk_frames; cf0 += nwave) {
+    const int cf = cf0 + wave;
+    const bool q_ok = pos_ok && cf < p.chunk_frames;
+    const int q_row = min(cf, p.chunk_frames - 1) * S + min(pr, fh - 1) * fw + min(pc, fw - 1);
+    const uint16_t* qp = (const uint16_t*)p.q + (int64_t)q_row * p.tok_stride + (int64_t)e.head * D;
+    u32x4 qreg[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qreg[ks] = *(const u32x4*)(qp + ks * 16 + half * 8);
+
+    AttnState<D> st;
+    st.init();
+    if (n_tiles > 0) {
+      load(0);
+      store(0, 0);
+    }
+    __syncthreads();
+    for (int t = 0; t < n_tiles; ++t) {
+      const bool more = t + 1 < n_tiles;
+      if (more) load(t + 1);
+      const uint16_t* buf = lds + (t & 1) * L::bufElems;
+      const int* kcd = kcoord[t & 1];
+      int kr4[2][4][4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int4 v = *(const int4*)(kcd + kb * 32 + 8 * a + 4 * half);
+          kr4[kb][a][0] = v.x;
+          kr4[kb][a][1] = v.y;
+          kr4[kb][a][2] = v.z;
+          kr4[kb][a][3] = v.w;
+        }
+      attend_tile<D, true>(st, qreg, buf, p.scale_log2, l32, half, [&](int kb, int r) {
+        const int kc2 = kr4[kb][r >> 2][r & 3];
+        const unsigned dr = (unsigned)((kc2 >> 16) - r0q);
+        const unsigned dc = (unsigned)((kc2 & 0xFFFF) - c0q);
+        return dr < (unsigned)eh && dc < (unsigned)ew;
+      });
+      if (more) store(t + 1, (t + 1) & 1);
+      __syncthreads();
+    }
+
+    const float l_tot = sum_halves(st.l_run);
+    if (q_ok) {
+      if (e.out_slot >= 0) {
+        const int64_t prow = (int64_t)e.out_slot * p.lq + q_row;
+        store_partial<D>(st, l_tot, p.part_o + prow * D, p.part_ml + prow * 2, half);
+      } else {
+        // merge with the dense current-block partial by log-sum-exp
+        const int64_t crow = (int64_t)e.cur_slot * p.lq + q_row;
+        const float m_c = p.part_ml[crow * 2], l_c = p.part_ml[crow * 2 + 1];
+        const float M = fmaxf(st.m_run, m_c);
+        const float wa = st.m_run == -INFINITY ? 0.f : fast_exp2(st.m_run - M);
+        const float wc = fast_exp2(m_c - M);
+        const float inv = 1.0f / (wa * l_tot + wc * l_c);
+        const float* po = p.part_o + crow * D;
+        uint16_t* op = (uint16_t*)p.out + (int64_t)q_row * p.tok_stride + (int64_t)e.head * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const int d = db * 32 + 8 * a + 4 * half;
+            const f32x4 oc = *(const f32x4*)(po + d);
+            u32x2 w;
+            w[0] = pack_bf16((wa * st.o[db][4 * a] + wc * oc[0]) * inv,
+                             (wa * st.o[db][4 * a + 1] + wc * oc[1]) * inv);
+            w[1] = pack_bf16((wa * st.o[db][4 * a + 2] + wc * oc[2]) * inv,
+                             (wa * st.o[db][4 * a + 3] + wc * oc[3]) * inv);
+            *(u32x2*)(op + d) = w;
+          }
+      }
+    }
+  }
+}
+
+__global__ void gather_origins_kernel(int fh, int fw, int gh, int gw, int32_t* out) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= fh * fw) return;
+  out[2 * t] = win_origin(t / fw, gh, fh);
+  out[2 * t + 1] = win_origin(t % fw, gw, fw);
+}
+
+}  // namespace
+
+hipError_t launch_spatial_f32(const SpatialParams& p, int head_dim, hipStream_t s);
+
+hipError_t launch_spatial(const SpatialParams& p, int head_dim, int bf16, hipStream_t s) {
+  if (p.n_entries == 0) return hipSuccess;
+  if (!bf16) return launch_spatial_f32(p, head_dim, s);
+  const dim3 grid(p.tiles_r * p.tiles_c, p.n_entries), block(256);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(spatial_attn_bf16<128>, grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL(spatial_attn_bf16<64>, grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_origins(int frame_h, int frame_w, int grid_h, int grid_w, int32_t* out,
+                                 hipStream_t s) {
+  const int n = frame_h * frame_w;
+  hipLaunchKernelGGL(gather_origins_kernel, dim3((n + 255) / 256), dim3(256), 0, s, frame_h, frame_w,
+                     grid_h, grid_w, out);
+  return hipGetLastError();
+}
+
+}  // namespace hc

@@ -1,0 +1,42 @@
+"""Helpers shared by the GPU tests: moving seeded inputs to the device and picking
+query rows for sampled parity checks."""
+import numpy as np
+import torch
+
+
+def dev(a, dtype):
+    """float32 numpy array (holding bf16 values for bf16) -> device tensor."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16 if dtype == "bf16" else torch.float32).cuda()
+
+
+def to_device(inp):
+    g = inp.geom
+    return dict(q=dev(inp.q, g.dtype), k_hist=dev(inp.k_hist, g.dtype), v_hist=dev(inp.v_hist, g.dtype),
+                k_cur=dev(inp.k_cur, g.dtype), v_cur=dev(inp.v_cur, g.dtype))
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def sample_rows(geom, n_random=256, seed=0):
+    """Frame corners, edge midpoints and the centre of every chunk frame, plus random rows."""
+    S, fh, fw = geom.tokens_per_frame, geom.frame_h, geom.frame_w
+    pts = [(0, 0), (0, fw - 1), (fh - 1, 0), (fh - 1, fw - 1), (0, fw // 2), (fh - 1, fw // 2),
+           (fh // 2, 0), (fh // 2, fw - 1), (fh // 2, fw // 2), (1, 1), (fh - 2, fw - 2)]
+    rows = {f * S + r * fw + c for f in range(geom.chunk_frames) for r, c in pts if 0 <= r < fh and 0 <= c < fw}
+    rng = np.random.default_rng(seed)
+    rows |= set(rng.integers(0, geom.lq, size=n_random).tolist())
+    return np.array(sorted(rows))
+
+
+def assert_close(got, want, max_abs, mean_abs, what=""):
+    err = np.abs(got - want)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    assert err.max() <= max_abs, f"{what}: max-abs {err.max():.3e} > {max_abs}"
+    assert err.mean() <= mean_abs, f"{what}: mean-abs {err.mean():.3e} > {mean_abs}"
+    return float(err.max()), float(err.mean())
+
+
+TOL = {"bf16": (1e-2, 1e-3), "f32": (1e-4, 1e-5)}

@@ -1,0 +1,253 @@
+"""GPU parity of the HIP path against the CPU fp64 oracle, through the C ABI.
+
+Bit-exact: buffer contents, slot tables, Spatial window origins, labels.
+Floating point (outputs against the oracle on the same bf16-rounded inputs):
+max-abs <= 1e-2 and mean-abs <= 1e-3 for bf16; max-abs <= 1e-4 for fp32 inputs.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import TOL, assert_close, dev, host, sample_rows, to_device
+from head_routed_sparse_amd import headcast as hc
+from head_routed_sparse_amd import inputs as hin
+from oracle import headcast_oracle as orc
+
+pytestmark = pytest.mark.gpu
+S_, D_, P_, G_ = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hc.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_routed(inp, labels=None):
+    g = inp.geom
+    labels = inp.labels if labels is None else labels
+    t = to_device(inp)
+    d = hc.make_desc(g)
+    buf = hc.hc_build_head_buffers(d, labels, t["k_hist"], t["v_hist"], inp.n_hist_frames)
+    out = hc.hc_routed_attention(buf, t["q"], t["k_cur"], t["v_cur"])
+    torch.cuda.synchronize()
+    return host(out), buf, t
+
+
+GEOMS = {
+    # several query tiles with a ragged tail, several key tiles with a ragged tail
+    "10x13_C2_F8_d128": hin.Geometry(4, 128, 10, 13, 2, 8, 3, 3, "bf16"),
+    "9x17_C3_F12_d64": hin.Geometry(4, 64, 9, 17, 3, 12, 4, 4, "bf16"),
+    "tiny_bf16": hin.Geometry(4, 64, 8, 8, 1, 5, 3, 3, "bf16"),
+    "tiny_f32": hin.CONFIGS["tiny"]["geom"],
+    "7x20_C1_F6_d128_f32": hin.Geometry(4, 128, 7, 20, 1, 6, 5, 2, "f32"),
+}
+
+
+@pytest.mark.parametrize("gname", list(GEOMS))
+@pytest.mark.parametrize("labels", [(S_, D_, P_, G_), (G_, G_, G_, G_), (P_, P_, S_, D_)])
+def test_routed_matches_oracle(gname, labels):
+    g = GEOMS[gname]
+    inp = hin.generate(g, labels, seed=zlib.crc32(gname.encode()) % 1000)
+    got, _, _ = run_routed(inp)
+    want = orc.routed_attention(inp)
+    print(gname, labels, assert_close(got, want, *TOL[g.dtype], what=f"{gname} {labels}"))
+
+
+@pytest.mark.parametrize("n_hist", [0, 2, 4])
+def test_routed_partial_window(n_hist):
+    g = hin.Geometry(4, 128, 6, 11, 2, 10, 3, 3, "bf16")
+    inp = hin.generate(g, (S_, D_, P_, G_), seed=3, n_hist_frames=n_hist)
+    got, _, _ = run_routed(inp)
+    want = orc.routed_attention(inp)
+    assert_close(got, want, *TOL["bf16"], what=f"n_hist={n_hist}")
+
+
+@pytest.mark.parametrize("grid", [(1, 1), (2, 2), (8, 8), (12, 40), (3, 6)])
+def test_spatial_grids(grid):
+    g = hin.Geometry(2, 128, 9, 14, 2, 8, grid[0], grid[1], "bf16")
+    inp = hin.generate(g, (P_, P_), seed=4)
+    got, _, _ = run_routed(inp)
+    assert_close(got, orc.routed_attention(inp), *TOL["bf16"], what=f"grid={grid}")
+    if grid[0] >= g.frame_h and grid[1] >= g.frame_w:     # full-frame window == Global
+        got_g, _, _ = run_routed(inp, labels=(G_, G_))
+        assert_close(got, got_g, 2e-3, 2e-4, what="spatial==global")
+
+
+def test_one_block_window_all_paths_agree():
+    g = hin.Geometry(4, 128, 7, 9, 2, 2, 3, 3, "bf16")
+    inp = hin.generate(g, (S_, D_, P_, G_), seed=5)
+    got, _, _ = run_routed(inp)
+    want = orc.routed_attention(inp)
+    assert_close(got, want, *TOL["bf16"])
+    for h in range(4):     # with no history every class sees exactly the current block
+        assert_close(got[:, h], orc.path_attention(inp, h, G_), *TOL["bf16"])
+
+
+def test_zero_query_key_set_moments():
+    """q = 0 gives the mean of V over the key set: V columns (1, frame, row, col, row^2,
+    col^2) pin every path's membership on the GPU (values exact in bf16)."""
+    g = hin.Geometry(4, 128, 6, 11, 2, 10, 3, 3, "bf16")
+    inp = hin.generate(g, (S_, D_, P_, G_), seed=6)
+    inp.q[:] = 0
+    S = g.tokens_per_frame
+    n = (inp.n_hist_frames + g.chunk_frames) * S
+    t = np.arange(n)
+    f, r, c = t // S, (t % S) // g.frame_w, t % g.frame_w
+    cols = np.stack([np.ones(n), f, r, c, r * r, c * c], axis=1).astype(np.float32)
+    v = np.zeros((n, g.num_heads, g.head_dim), np.float32)
+    v[:, :, :6] = cols[:, None, :]
+    inp.v_hist[:] = v[: inp.n_hist_frames * S]
+    inp.v_cur[:] = v[inp.n_hist_frames * S:]
+    got, _, _ = run_routed(inp)
+    want = orc.routed_attention(inp)
+    rel = np.abs(got[:, :, :6] - want[:, :, :6]) / np.maximum(np.abs(want[:, :, :6]), 1.0)
+    assert rel.max() < 8e-3, rel.max()
+
+
+def test_gather_origins_bit_exact():
+    for fh, fw, gh, gw in [(30, 52, 8, 8), (45, 80, 8, 8), (68, 120, 8, 8), (8, 8, 3, 3), (5, 7, 9, 2), (9, 9, 4, 5)]:
+        d = hc.make_desc(hin.Geometry(1, 64, fh, fw, 1, 2, gh, gw, "bf16"))
+        got = hc.hc_debug_gather_origins(d, gh, gw).cpu().numpy()
+        pos = np.arange(fh * fw)
+        want = np.stack([orc.window_origin(pos // fw, gh, fh), orc.window_origin(pos % fw, gw, fw)], axis=1)
+        assert np.array_equal(got, want), (fh, fw, gh, gw)
+
+
+def buffer_rows(buf, head, which):
+    """Rows of head's K or V buffer region as float64 [rows][d]."""
+    k_off, v_off, rows = hc.hc_debug_head_region(buf, head)
+    if rows == 0:
+        return np.zeros((0, buf.desc.head_dim))
+    off = k_off if which == "k" else v_off
+    es = 2 if buf.desc.dtype == hc.HC_BF16 else 4
+    raw = buf.memory[off: off + rows * buf.desc.head_dim * es]
+    t = raw.view(torch.bfloat16 if es == 2 else torch.float32).reshape(rows, buf.desc.head_dim)
+    return host(t)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_build_and_append_bit_exact(dtype):
+    g = hin.Geometry(4, 64, 3, 5, 2, 10, 2, 2, dtype)     # R = 3 rolling blocks
+    labels = (S_, D_, P_, G_)
+    C, S = g.chunk_frames, g.tokens_per_frame
+    rng = np.random.default_rng(7)
+    n_blocks = 10
+    chunks = [hin.round_to_bf16(rng.standard_normal((2, C * S, 4, 64), dtype=np.float32)) for _ in range(n_blocks)]
+    n0 = 2                                                  # build from blocks 0, 1
+    k_hist = np.concatenate([chunks[b][0] for b in range(n0)])
+    v_hist = np.concatenate([chunks[b][1] for b in range(n0)])
+    buf = hc.hc_build_head_buffers(hc.make_desc(g), labels, dev(k_hist, dtype), dev(v_hist, dtype), n0 * C)
+    for nb in range(n0, n_blocks + 1):
+        torch.cuda.synchronize()
+        table = orc.slot_table(labels, g.window_frames, C, nb)
+        assert np.array_equal(hc.hc_debug_slot_table(buf), table)
+        for h in range(4):
+            for which, idx in (("k", 0), ("v", 1)):
+                rows = buffer_rows(buf, h, which)
+                for pos in range(rows.shape[0] // S):
+                    fr = table[h, pos]
+                    if fr < 0:
+                        continue
+                    b, i = divmod(int(fr), C)
+                    want = chunks[b][idx][i * S:(i + 1) * S, h, :]
+                    assert np.array_equal(rows[pos * S:(pos + 1) * S], want), (nb, h, pos)
+        if nb < n_blocks:
+            hc.hc_append_chunk(buf, dev(chunks[nb][0], dtype), dev(chunks[nb][1], dtype))
+    assert hc.hc_buffers_state(buf) == n_blocks
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rollout_routed_matches_oracle_window(dtype):
+    """Warm-up from an empty cache, then one block per step: after every append the
+    routed output equals the oracle on the logical window (sink block + recent blocks)."""
+    g = hin.Geometry(4, 128 if dtype == "bf16" else 64, 5, 9, 2, 8, 3, 3, dtype)
+    labels = (S_, D_, P_, G_)
+    C, S, H, d = g.chunk_frames, g.tokens_per_frame, g.num_heads, g.head_dim
+    rng = np.random.default_rng(8)
+    blocks = [hin.round_to_bf16(rng.standard_normal((3, C * S, H, d), dtype=np.float32)) for _ in range(7)]
+    buf = hc.hc_build_head_buffers(hc.make_desc(g), labels, None, None, 0)
+    ws = hc.routed_workspace(buf)
+    for step in range(7):
+        q, k, v = blocks[step]
+        out = host(hc.hc_routed_attention(buf, dev(q, dtype), dev(k, dtype), dev(v, dtype), workspace=ws))
+        hist = orc.window_history_blocks(step, g.window_frames, C)
+        kh = np.concatenate([blocks[b][1] for b in hist]) if hist else np.zeros((0, H, d), np.float32)
+        vh = np.concatenate([blocks[b][2] for b in hist]) if hist else np.zeros((0, H, d), np.float32)
+        inp = hin.LayerInputs(g, np.array(labels, np.int32), q, kh, vh, k, v, len(hist) * C)
+        assert_close(out, orc.routed_attention(inp), *TOL[dtype], what=f"step {step}")
+        hc.hc_append_chunk(buf, dev(k, dtype), dev(v, dtype))
+
+
+@pytest.mark.parametrize("name", ["480p", "720p", "1080p"])
+def test_full_size_sampled_rows(name):
+    """The benchmark's workloads at full size; sampled query rows against the oracle,
+    plus the all-Global call of the same kernel."""
+    inp = hin.config_inputs(name)
+    g = inp.geom
+    t = to_device(inp)
+    d = hc.make_desc(g)
+    rows = sample_rows(g, n_random=192, seed=1)
+    for labels in (inp.labels, np.full(g.num_heads, G_, np.int32)):
+        buf = hc.hc_build_head_buffers(d, labels, t["k_hist"], t["v_hist"], inp.n_hist_frames)
+        out = host(hc.hc_routed_attention(buf, t["q"], t["k_cur"], t["v_cur"]))
+        want = orc.routed_attention(inp, labels=labels, rows=rows)
+        print(name, labels, assert_close(out[rows], want, *TOL["bf16"], what=name))
+        assert np.isfinite(out).all()
+        del buf
+
+
+def test_deterministic_bitwise():
+    inp = hin.config_inputs("480p")
+    a, _, _ = run_routed(inp)
+    b, _, _ = run_routed(inp)
+    assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------------------- classification
+def classify_gpu(inp, **params):
+    g = inp.geom
+    t = to_device(inp)
+    p = hc.hc_default_classify_params(**params)
+    return hc.hc_classify_heads(hc.make_desc(g), p, t["q"], t["k_hist"], t["v_hist"], inp.n_hist_frames,
+                                t["k_cur"], t["v_cur"])
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_classify_planted_matches_oracle(dtype, d):
+    g = hin.Geometry(8, d, 12, 20, 3, 21, 8, 8, dtype)
+    labels = [S_, D_, P_, G_, G_, P_, D_, S_]
+    inp = hin.generate(g, labels, seed=5, planted=True)
+    got, stats = classify_gpu(inp, gamma=0.5)
+    want, ost = orc.classify_heads(inp, dict(gamma=0.5))
+    assert list(want) == labels
+    assert list(got) == labels
+    for h in range(8):
+        o = ost[h]
+        ref = [o["cos_sink"], o["cos_dummy"], o["cos_spatial"], o["p5"], o["mse"], o["score"]]
+        assert np.allclose(stats[h], ref, atol=2e-3), (h, stats[h], ref)
+
+
+def test_classify_unplanted_statistics_match_oracle():
+    g = hin.Geometry(4, 128, 9, 14, 2, 8, 3, 3, "bf16")
+    inp = hin.generate(g, [G_] * 4, seed=9)
+    got, stats = classify_gpu(inp)
+    want, ost = orc.classify_heads(inp)
+    assert list(got) == list(want)
+    for h in range(4):
+        o = ost[h]
+        ref = [o["cos_sink"], o["cos_dummy"], o["cos_spatial"], o["p5"], o["mse"], o["score"]]
+        assert np.allclose(stats[h], ref, atol=3e-3), (h, stats[h], ref)
+
+
+def test_classify_sink_proxy_variant():
+    g = hin.Geometry(2, 128, 12, 20, 3, 21, 8, 8, "bf16")
+    inp = hin.generate(g, [D_, G_], seed=6, planted=True)
+    got, _ = classify_gpu(inp, gamma=0.5, sink_proxy_includes_current=1)
+    want, _ = orc.classify_heads(inp, dict(gamma=0.5, sink_proxy_includes_current=True))
+    assert list(got) == list(want) == [S_, G_]
