@@ -1,0 +1,226 @@
+"""Benchmark of the head-routed attention step on one MI355X.
+
+A step is one routed attention call for one layer and one denoise step: host routing,
+the dense varlen kernel (Sink / Dummy / Global heads and the current block of the
+Spatial heads), the split merge and the Spatial history gather. Inputs are seeded
+synthetic tensors already resident in HBM. The headline workload is the 720P-shaped
+layer; the same kernel with every head Global is the full-window baseline, and the
+1080P-shaped layer is reported beside it.
+
+Prints one JSON line (rank 0). Usage: python bench.py [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed-attn ms/layer-step + speedup vs full-window attn at 720P/1080P, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="720p", choices=["480p", "720p", "1080p"])
+    ap.add_argument("--second", default="1080p", help="second workload reported beside ('' = none)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=384, help="query rows per head in the CPU sample")
+    return ap.parse_args()
+
+
+def dense_flops(geom, labels, n_hist):
+    """Algorithmic flops of the dense kernel: 4 * Lq * Lk * d per head (QK^T and PV)."""
+    S, C, lq, d = geom.tokens_per_frame, geom.chunk_frames, geom.lq, geom.head_dim
+    tot = 0
+    for cls in labels:
+        hist = {0: min(n_hist, C), 1: 0, 2: 0, 3: n_hist}[int(cls)] * S
+        tot += 4.0 * lq * (hist + C * S) * d
+    return tot
+
+
+def spatial_work(geom, labels, n_hist):
+    """(flops, unique bytes) of the Spatial history gather: every query against
+    n_hist * g^2 keys; bytes = history K+V once + Q + O, bf16."""
+    n_sp = int(np.sum(np.asarray(labels) == 2))
+    g2 = min(geom.grid_h, geom.frame_h) * min(geom.grid_w, geom.frame_w)
+    flops = 4.0 * geom.lq * n_hist * g2 * geom.head_dim * n_sp
+    byts = n_sp * (2 * n_hist * geom.tokens_per_frame * geom.head_dim * 2 + 2 * geom.lq * geom.head_dim * 2)
+    return flops, byts
+
+
+def time_calls(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def measure(name, steps, warmup, with_events):
+    import torch
+    from head_routed_sparse_amd import headcast as hc
+    from head_routed_sparse_amd import inputs as hin
+    inp = hin.config_inputs(name)
+    g = inp.geom
+
+    def dev(a):
+        return torch.from_numpy(a).to(torch.bfloat16).cuda()
+
+    q, kh, vh, kc, vc = (dev(a) for a in (inp.q, inp.k_hist, inp.v_hist, inp.k_cur, inp.v_cur))
+    desc = hc.make_desc(g)
+    res = {}
+    for tag, labels in (("routed", inp.labels), ("all_global", np.full(g.num_heads, 3, np.int32))):
+        buf = hc.hc_build_head_buffers(desc, labels, kh, vh, inp.n_hist_frames)
+        ws = hc.routed_workspace(buf)
+        out = torch.empty_like(q)
+        fn = lambda: hc.hc_routed_attention(buf, q, kc, vc, out=out, workspace=ws)  # noqa: E731
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        if with_events:
+            hc.hc_timing_read()
+            hc.hc_timing_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        kern = {}
+        if with_events:
+            hc.hc_timing_enable(False)
+            kern = {k: (v[0] / max(v[1], 1), v[1]) for k, v in hc.hc_timing_read().items() if v[1]}
+        res[tag] = dict(ms=ms, kernels=kern, labels=labels)
+        del buf, ws, out
+    # one-time costs beside the step: buffer build, one append, classification
+    from head_routed_sparse_amd.headcast import hc_default_classify_params
+    buf_bytes = hc.hc_head_buffers_bytes(desc, inp.labels)
+    mem = torch.empty(buf_bytes, dtype=torch.uint8, device="cuda")
+    res["build_ms"] = time_calls(lambda: hc.hc_build_head_buffers(desc, inp.labels, kh, vh, inp.n_hist_frames,
+                                                                  memory=mem), 3, 1)
+    buf = hc.hc_build_head_buffers(desc, inp.labels, kh, vh, inp.n_hist_frames, memory=mem)
+    res["append_ms"] = time_calls(lambda: hc.hc_append_chunk(buf, kc, vc), 6, 2)
+    p = hc_default_classify_params(gamma=0.5)
+    ws = torch.empty(hc.hc_classify_workspace_bytes(desc, p, inp.n_hist_frames), dtype=torch.uint8, device="cuda")
+    res["classify_ms"] = time_calls(lambda: hc.hc_classify_heads(desc, p, q, kh, vh, inp.n_hist_frames, kc, vc,
+                                                                 workspace=ws), 2, 1)
+    res["kv_bytes_routed"] = buf_bytes
+    res["kv_bytes_monolithic"] = 2 * g.hist_frames * g.tokens_per_frame * g.num_heads * g.head_dim * 2
+    res["geom"] = g
+    res["inp"] = inp
+    return res
+
+
+def cpu_baseline(inp, rows_per_head):
+    """The oracle as it stands, on a sample of query rows of every head; scaled to
+    ms per layer-step by the fraction of rows computed."""
+    from oracle import headcast_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    g = inp.geom
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(g.lq, size=min(rows_per_head, g.lq), replace=False))
+    t0 = time.perf_counter()
+    orc.routed_attention(inp, rows=rows)
+    dt = time.perf_counter() - t0
+    ms = dt * 1e3 * g.lq / rows.size
+    return dict(value=round(ms, 1), unit="ms/layer-step", cores=int(cores), kind="oracle",
+                sample=f"{rows.size} of {g.lq} query rows per head, all {g.num_heads} heads, "
+                       f"{g.frame_h}x{g.frame_w} layer (fp64 numpy, {dt:.1f} s), scaled by rows")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the routed step shards over heads, but this build "
+              "runs on a single MI355X only (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from head_routed_sparse_amd import headcast as hc
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    hc.lib()
+    print(f"[bench] workload {a.config}: warmup {a.warmup}, steps {a.steps}", file=sys.stderr, flush=True)
+    main_res = measure(a.config, a.steps, a.warmup, with_events=True)
+    g = main_res["geom"]
+    n_hist = g.hist_frames
+    r, base = main_res["routed"], main_res["all_global"]
+    dense_ms = r["kernels"]["dense"][0]
+    dflops = dense_flops(g, r["labels"], n_hist)
+    achieved = dflops / (dense_ms * 1e-3) / 1e12
+    sp_flops, sp_bytes = spatial_work(g, r["labels"], n_hist)
+    out = {
+        "metric": METRIC,
+        "value": round(r["ms"], 4),
+        "unit": "ms/layer-step",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(r["ms"], 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{a.config} single layer, one denoise step: {g.num_heads} heads d={g.head_dim}, "
+                               f"{g.frame_h}x{g.frame_w} latent frames, block {g.chunk_frames} frames, window "
+                               f"{g.window_frames} frames, grid {g.grid_h}x{g.grid_w}, mix sink/dummy/spatial/global "
+                               f"{[int((r['labels'] == c).sum()) for c in range(4)]}",
+                   "global_batch": 1, "seq_len": g.lq, "parallelism": "none (1 GPU)"},
+        "speedup_vs_full_window": round(base["ms"] / r["ms"], 3),
+        "full_window_ms": round(base["ms"], 4),
+        "kernel_avg_ms": {k: round(v[0], 4) for k, v in r["kernels"].items()},
+        "full_window_kernel_avg_ms": {k: round(v[0], 4) for k, v in base["kernels"].items()},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "dense_attn_bf16<128>", "flops_per_launch": dflops},
+        "full_window_roofline_frac": round(dense_flops(g, base["labels"], n_hist) /
+                                           (base["kernels"]["dense"][0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "spatial_gather": {"flops": sp_flops, "unique_bytes": sp_bytes,
+                           "avg_ms": round(r["kernels"].get("spatial", (0, 0))[0], 4),
+                           "hbm_frac": round(sp_bytes / (r["kernels"]["spatial"][0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+                           if "spatial" in r["kernels"] else None},
+        "one_time_ms": {"build_buffers": round(main_res["build_ms"], 3), "append_chunk": round(main_res["append_ms"], 3),
+                        "classify_heads": round(main_res["classify_ms"], 3)},
+        "kv_cache_bytes": {"per_head_buffers": main_res["kv_bytes_routed"],
+                           "monolithic": main_res["kv_bytes_monolithic"]},
+        "context_pages_end_to_end_speedup": {"720p": 1.62, "1080p": 1.95, "hardware": "unnamed single GPU"},
+    }
+    if a.second:
+        print(f"[bench] second workload {a.second}", file=sys.stderr, flush=True)
+        sec = measure(a.second, max(3, a.steps // 2), 2, with_events=True)
+        gs = sec["geom"]
+        out["second_workload"] = {
+            "workload": a.second, "routed_ms": round(sec["routed"]["ms"], 4),
+            "full_window_ms": round(sec["all_global"]["ms"], 4),
+            "speedup_vs_full_window": round(sec["all_global"]["ms"] / sec["routed"]["ms"], 3),
+            "dense_roofline_frac": round(dense_flops(gs, sec["routed"]["labels"], gs.hist_frames) /
+                                         (sec["routed"]["kernels"]["dense"][0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "classify_ms": round(sec["classify_ms"], 3)}
+        del sec
+    if not a.no_cpu:
+        print("[bench] cpu oracle sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(main_res["inp"], a.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -57,34 +57,40 @@ __global__ __launch_bounds__(256, 2) void dense_attn_bf16(const DenseParams p) {
   const int n_tiles = (k_end - k_begin + kKeyTile - 1) / kKeyTile;
   TileRegs<D> regs;
   auto load = [&](int k0) {
-    auto kp = [&](int j) {
-      const int kk = min(k0 + j, k_end - 1);
-      return kk < hl ? kh + (int64_t)kk * hs : kc + (int64_t)(kk - hl) * ts;
-    };
-    auto vp = [&](int j) {
-      const int kk = min(k0 + j, k_end - 1);
-      return kk < hl ? vh + (int64_t)kk * hs : vc + (int64_t)(kk - hl) * ts;
-    };
-    load_tile<D>(regs, kp, vp, tid);
+    if (k0 + kKeyTile <= min(hl, k_end)) {            // whole tile in the history segment
+      load_tile_rows<D>(regs, kh + (int64_t)k0 * hs, vh + (int64_t)k0 * hs, hs, tid);
+    } else if (k0 >= hl && k0 + kKeyTile <= k_end) {  // whole tile in the current block
+      load_tile_rows<D>(regs, kc + (int64_t)(k0 - hl) * ts, vc + (int64_t)(k0 - hl) * ts, ts, tid);
+    } else {                                           // straddles the segments or the end
+      auto kp = [&](int j) {
+        const int kk = min(k0 + j, k_end - 1);
+        return kk < hl ? kh + (int64_t)kk * hs : kc + (int64_t)(kk - hl) * ts;
+      };
+      auto vp = [&](int j) {
+        const int kk = min(k0 + j, k_end - 1);
+        return kk < hl ? vh + (int64_t)kk * hs : vc + (int64_t)(kk - hl) * ts;
+      };
+      load_tile<D>(regs, kp, vp, tid);
+    }
   };
   load(k_begin);
   store_tile<D>(regs, lds, tid);
   __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
+  // every tile but the last is full: one straight-line loop body
+  for (int t = 0; t + 1 < n_tiles; ++t) {
     const int k0 = k_begin + t * kKeyTile;
-    const bool more = t + 1 < n_tiles;
-    if (more) load(k0 + kKeyTile);
-    const uint16_t* buf = lds + (t & 1) * L::bufElems;
-    if (k0 + kKeyTile > k_end) {
-      const int valid = k_end - k0;
-      attend_tile<D, true>(st, qreg, buf, p.scale_log2, l32, half,
-                           [&](int kb, int r) { return score_key(kb, r, half) < valid; });
-    } else {
-      attend_tile<D, false>(st, qreg, buf, p.scale_log2, l32, half, [](int, int) { return true; });
-    }
-    if (more) store_tile<D>(regs, lds + ((t + 1) & 1) * L::bufElems, tid);
+    load(k0 + kKeyTile);
+    attend_tile<D, false>(st, qreg, lds + (t & 1) * L::bufElems, p.scale_log2, l32, half,
+                          [](int, int) { return true; });
+    store_tile<D>(regs, lds + ((t + 1) & 1) * L::bufElems, tid);
     __syncthreads();
+  }
+  if (n_tiles > 0) {   // last tile, possibly ragged
+    const int t = n_tiles - 1;
+    const int valid = k_end - (k_begin + t * kKeyTile);
+    attend_tile<D, true>(st, qreg, lds + (t & 1) * L::bufElems, p.scale_log2, l32, half,
+                         [&](int kb, int r) { return score_key(kb, r, half) < valid; });
   }
 
   const float l_tot = sum_halves(st.l_run);

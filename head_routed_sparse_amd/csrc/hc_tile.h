@@ -52,6 +52,27 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& t, KPtr kptr, VPtr vptr, 
   }
 }
 
+// Fast path: the tile's 64 rows are consecutive rows base[0..63] with a fixed stride.
+template <int D>
+__device__ __forceinline__ void load_tile_rows(TileRegs<D>& t, const uint16_t* kbase, const uint16_t* vbase,
+                                               int64_t stride, int tid) {
+  constexpr int cpr = TileRegs<D>::cpr;
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::kChunks; ++i) {
+    const int idx = tid + 256 * i;
+    t.k[i] = *(const u32x4*)(kbase + (int64_t)(idx / cpr) * stride + (idx % cpr) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::vPer; ++i) {
+    const int u = tid + 256 * i;
+    if (u < TileRegs<D>::vUnits) {
+      const int g = u / cpr, ch = u % cpr;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) t.v[i][j] = *(const u32x4*)(vbase + (int64_t)(4 * g + j) * stride + ch * 8);
+    }
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void store_tile(const TileRegs<D>& t, uint16_t* buf, int tid) {
   using L = AttnLds<D>;
