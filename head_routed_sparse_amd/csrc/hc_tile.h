@@ -26,7 +26,9 @@ template <int D>
 struct TileRegs {
   static constexpr int cpr = D / 8;                        // 16-B chunks per row
   static constexpr int kChunks = kKeyTile * cpr / 256;     // K chunks per thread
-  static constexpr int vUnits = (kKeyTile / 4) * cpr;      // (4 keys x 8 d) units
+  // (4 keys x 8 d) units; unit u = key group u % 16, d chunk u / 16, so that the 16 lanes
+  // of one LDS write group hit 16 different bank pairs of the transposed tile
+  static constexpr int vUnits = (kKeyTile / 4) * cpr;
   static constexpr int vPer = (vUnits + 255) / 256;
   u32x4 k[kChunks];
   u32x4 v[vPer][4];
@@ -45,7 +47,7 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& t, KPtr kptr, VPtr vptr, 
   for (int i = 0; i < TileRegs<D>::vPer; ++i) {
     const int u = tid + 256 * i;
     if (u < TileRegs<D>::vUnits) {
-      const int g = u / cpr, ch = u % cpr;
+      const int g = u % 16, ch = u / 16;   // 16-lane groups: one d chunk, all key groups
 #pragma unroll
       for (int j = 0; j < 4; ++j) t.v[i][j] = *(const u32x4*)(vptr(4 * g + j) + ch * 8);
     }
@@ -66,7 +68,7 @@ __device__ __forceinline__ void load_tile_rows(TileRegs<D>& t, const uint16_t* k
   for (int i = 0; i < TileRegs<D>::vPer; ++i) {
     const int u = tid + 256 * i;
     if (u < TileRegs<D>::vUnits) {
-      const int g = u / cpr, ch = u % cpr;
+      const int g = u % 16, ch = u / 16;   // 16-lane groups: one d chunk, all key groups
 #pragma unroll
       for (int j = 0; j < 4; ++j) t.v[i][j] = *(const u32x4*)(vbase + (int64_t)(4 * g + j) * stride + ch * 8);
     }
@@ -87,7 +89,7 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& t, uint16_t* buf, 
   for (int i = 0; i < TileRegs<D>::vPer; ++i) {
     const int u = tid + 256 * i;
     if (u < TileRegs<D>::vUnits) {
-      const int g = u / cpr, ch = u % cpr;
+      const int g = u % 16, ch = u / 16;   // 16-lane groups: one d chunk, all key groups
       const int pos = vt_pos(4 * g);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {   // dword w of each key row holds d = 2w, 2w+1
