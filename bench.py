@@ -35,7 +35,11 @@ def parse():
     ap.add_argument("--config", default="720p", choices=["480p", "720p", "1080p"])
     ap.add_argument("--second", default="1080p", help="second workload reported beside ('' = none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=384, help="query rows per head in the CPU sample")
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="query rows per head in the CPU sample")
+    ap.add_argument("--only-routed", action="store_true",
+                    help="profiling runs: time only the routed call of the main workload")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run one plain device copy of MIB MiB (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -71,7 +75,7 @@ def time_calls(fn, steps, warmup):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
-def measure(name, steps, warmup, with_events):
+def measure(name, steps, warmup, with_events, only_routed=False):
     import torch
     from head_routed_sparse_amd import headcast as hc
     from head_routed_sparse_amd import inputs as hin
@@ -84,7 +88,10 @@ def measure(name, steps, warmup, with_events):
     q, kh, vh, kc, vc = (dev(a) for a in (inp.q, inp.k_hist, inp.v_hist, inp.k_cur, inp.v_cur))
     desc = hc.make_desc(g)
     res = {}
-    for tag, labels in (("routed", inp.labels), ("all_global", np.full(g.num_heads, 3, np.int32))):
+    runs = [("routed", inp.labels)]
+    if not only_routed:
+        runs.append(("all_global", np.full(g.num_heads, 3, np.int32)))
+    for tag, labels in runs:
         buf = hc.hc_build_head_buffers(desc, labels, kh, vh, inp.n_hist_frames)
         ws = hc.routed_workspace(buf)
         out = torch.empty_like(q)
@@ -106,6 +113,10 @@ def measure(name, steps, warmup, with_events):
             kern = {k: (v[0] / max(v[1], 1), v[1]) for k, v in hc.hc_timing_read().items() if v[1]}
         res[tag] = dict(ms=ms, kernels=kern, labels=labels)
         del buf, ws, out
+    res["geom"] = g
+    res["inp"] = inp
+    if only_routed:
+        return res
     # one-time costs beside the step: buffer build, one append, classification
     from head_routed_sparse_amd.headcast import hc_default_classify_params
     buf_bytes = hc.hc_head_buffers_bytes(desc, inp.labels)
@@ -159,8 +170,25 @@ def main():
         sys.exit(2)
     hc.lib()
     print(f"[bench] workload {a.config}: warmup {a.warmup}, steps {a.steps}", file=sys.stderr, flush=True)
-    main_res = measure(a.config, a.steps, a.warmup, with_events=True)
+    if a.copy_calibration:
+        n = a.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: {n} bytes read, {n} bytes written", file=sys.stderr, flush=True)
+        del src, dst
+    main_res = measure(a.config, a.steps, a.warmup, with_events=True, only_routed=a.only_routed)
     g = main_res["geom"]
+    if a.only_routed:
+        r = main_res["routed"]
+        dense_ms = r["kernels"]["dense"][0]
+        print(json.dumps({"workload": a.config, "routed_ms": round(r["ms"], 4),
+                          "kernel_avg_ms": {k: round(v[0], 4) for k, v in r["kernels"].items()},
+                          "dense_tflops": round(dense_flops(g, r["labels"], g.hist_frames) / (dense_ms * 1e-3) / 1e12, 1)}),
+              flush=True)
+        return
     n_hist = g.hist_frames
     r, base = main_res["routed"], main_res["all_global"]
     dense_ms = r["kernels"]["dense"][0]

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <functional>
 #include <mutex>
@@ -213,6 +214,17 @@ void plan_splits(std::vector<Entry>& es, int nqt) {
   }
 }
 
+// Items of one key range (its query tiles) are dispatched consecutively; keeping a
+// run of them on one XCD lets them share the key range through that XCD's L2.
+int xcd_group_size(int nqt) {
+  static int forced = [] {
+    const char* e = getenv("HC_XCD_GROUP");
+    return e ? atoi(e) : 0;
+  }();
+  if (forced > 0) return forced;
+  return std::max(1, std::min(nqt, kXcdGroup));
+}
+
 // Launch dense entries (batched by kMaxEntries), longest items first.
 hc_status run_dense(std::vector<Entry> es, const DenseParams& base, int head_dim, int bf16, hipStream_t s,
                     int* n_items_out = nullptr) {
@@ -238,6 +250,7 @@ hc_status run_dense(std::vector<Entry> es, const DenseParams& base, int head_dim
     }
     p.n_entries = (int)n;
     p.n_items = items;
+    p.xcd_group = xcd_group_size(base.nqt);
     total_items += items;
     if (!n_items_out) {
       HC_HIP(timed(bf16 ? K_DENSE : K_F32, s, [&] { return launch_dense(p, head_dim, bf16, s); }));

@@ -20,7 +20,7 @@ __global__ __launch_bounds__(256, 2) void dense_attn_bf16(const DenseParams p) {
   constexpr int KS = D / 16;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * L::bufElems];
 
-  const int item = xcd_logical(blockIdx.x, kXcdGroup);
+  const int item = xcd_logical(blockIdx.x, p.xcd_group);
   if (item >= p.n_items) return;
   int ei = 0;
   while (ei + 1 < p.n_entries && item >= p.e[ei + 1].item_begin) ++ei;
@@ -106,8 +106,8 @@ __global__ __launch_bounds__(256, 2) void dense_attn_bf16(const DenseParams p) {
 
 }  // namespace
 
-int dense_items_grid(int n_items) {
-  const int span = 8 * kXcdGroup;
+int dense_items_grid(int n_items, int xcd_group) {
+  const int span = 8 * xcd_group;
   return (n_items + span - 1) / span * span;
 }
 
@@ -116,7 +116,7 @@ hipError_t launch_dense_f32(const DenseParams& p, int head_dim, hipStream_t s);
 hipError_t launch_dense(const DenseParams& p, int head_dim, int bf16, hipStream_t s) {
   if (p.n_items == 0) return hipSuccess;
   if (!bf16) return launch_dense_f32(p, head_dim, s);
-  const dim3 grid(dense_items_grid(p.n_items)), block(256);
+  const dim3 grid(dense_items_grid(p.n_items, p.xcd_group)), block(256);
   if (head_dim == 128)
     hipLaunchKernelGGL(dense_attn_bf16<128>, grid, block, 0, s, p);
   else

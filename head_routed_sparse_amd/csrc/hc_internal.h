@@ -45,7 +45,7 @@ struct DenseParams {
   int32_t n_entries;
   int32_t n_items;
   float scale_log2;      // softmax_scale * log2(e)
-  int32_t pad;
+  int32_t xcd_group;     // consecutive items kept on one XCD
   DenseEntry e[kMaxEntries];
 };
 
@@ -149,6 +149,6 @@ hipError_t launch_stats(const StatsParams& p, hipStream_t s);
 hipError_t launch_gather_origins(int frame_h, int frame_w, int grid_h, int grid_w, int32_t* out,
                                  hipStream_t s);
 
-int dense_items_grid(int n_items);   // workgroups launched for n_items (XCD-grouped padding)
+int dense_items_grid(int n_items, int xcd_group);   // workgroups for n_items (XCD-grouped padding)
 
 }  // namespace hc
