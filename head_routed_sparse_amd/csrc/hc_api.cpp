@@ -153,7 +153,7 @@ struct Entry {
   int32_t hist_len, cur_len, head, nsplit, split_len, slot;
 };
 
-constexpr int kSlotsPerCu = 2;    // dense workgroups resident per CU
+constexpr int kSlotsPerCu = 2;    // dense workgroups resident per CU (LDS-limited)
 constexpr int kNumCu = 256;
 constexpr double kItemOverheadTiles = 3.0;
 

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsParams p) {
 // One thread per query, exact online softmax in fp32; same item enumeration and
 // output conventions as the bf16 kernels (the output is fp32).
 template <int D>
-__global__ __launch_bounds__(128) void dense_attn_f32(const DenseParams p) {
+__global__ __launch_bounds__(kDenseQ) void dense_attn_f32(const DenseParams p) {
   const int item = blockIdx.x;
   if (item >= p.n_items) return;
   int ei = 0;
