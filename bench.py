@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--second", default="1080p", help="second workload reported beside ('' = none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="query rows per head in the CPU sample")
+    ap.add_argument("--no-full-step", dest="full_step", action="store_false",
+                    help="skip the 30-layer planted step")
     ap.add_argument("--only-routed", action="store_true",
                     help="profiling runs: time only the routed call of the main workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -159,6 +161,68 @@ def measure(name, steps, warmup, with_events, only_routed=False):
     return res
 
 
+def ablation(res, steps, warmup):
+    """Table-4 style speed ablation on the 720P layer: only the Spatial heads routed,
+    only the Sink and Dummy heads routed, all routed; the others stay Global."""
+    import torch
+    from head_routed_sparse_amd import headcast as hc
+    inp = res["inp"]
+    g = inp.geom
+    dev = lambda a: torch.from_numpy(a).to(torch.bfloat16).cuda()  # noqa: E731
+    q, kh, vh, kc, vc = (dev(a) for a in (inp.q, inp.k_hist, inp.v_hist, inp.k_cur, inp.v_cur))
+    desc = hc.make_desc(g)
+    lab = np.asarray(inp.labels)
+    variants = {"spatial_only": np.where(lab == 2, 2, 3), "sink_dummy_only": np.where(lab == 2, 3, lab)}
+    out = {"all_global_ms": round(res["all_global"]["ms"], 4), "full_ms": round(res["routed"]["ms"], 4)}
+    for name, labels in variants.items():
+        buf = hc.hc_build_head_buffers(desc, labels.astype(np.int32), kh, vh, inp.n_hist_frames)
+        ws = hc.routed_workspace(buf)
+        o = torch.empty_like(q)
+        ms = time_calls(lambda: hc.hc_routed_attention(buf, q, kc, vc, out=o, workspace=ws), steps, warmup)
+        out[name + "_ms"] = round(ms, 4)
+        del buf, ws, o
+    for k in list(out):
+        out[k.replace("_ms", "_speedup")] = round(res["all_global"]["ms"] / out[k], 3)
+    return out
+
+
+def full_step(steps, warmup):
+    """The 30-layer 720P step with planted heads: classify every layer once (labels
+    must equal the planted ones), build its buffers, then time one denoise step =
+    the routed call of every layer."""
+    import torch
+    from head_routed_sparse_amd import headcast as hc
+    from head_routed_sparse_amd import inputs as hin
+    cfg = hin.CONFIGS["full720p"]
+    g = cfg["geom"]
+    desc = hc.make_desc(g)
+    params = hc.hc_default_classify_params(gamma=0.5)
+    planted = hin.full_step_labels("full720p")
+    cws = torch.empty(hc.hc_classify_workspace_bytes(desc, params, g.hist_frames), dtype=torch.uint8, device="cuda")
+    layers, cls_ms, recovered = [], 0.0, 0
+    for layer in range(cfg["layers"]):
+        t = hin.full_step_layer_torch("full720p", layer)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        labels, _ = hc.hc_classify_heads(desc, params, t["q"], t["k_hist"], t["v_hist"], t["n_hist_frames"],
+                                         t["k_cur"], t["v_cur"], workspace=cws)
+        cls_ms += (time.perf_counter() - t0) * 1e3
+        recovered += int((labels == planted[layer]).sum())
+        buf = hc.hc_build_head_buffers(desc, labels, t["k_hist"], t["v_hist"], t["n_hist_frames"])
+        layers.append((buf, hc.routed_workspace(buf), t["q"], t["k_cur"], t["v_cur"], torch.empty_like(t["q"])))
+        del t
+    torch.cuda.synchronize()
+
+    def step():
+        for buf, ws, q, kc, vc, o in layers:
+            hc.hc_routed_attention(buf, q, kc, vc, out=o, workspace=ws)
+
+    ms = time_calls(step, steps, warmup)
+    return {"workload": "720p, 30 layers x 12 heads, planted heads 54/90/126/90",
+            "labels_recovered": f"{recovered}/{planted.size}", "classify_ms_all_layers": round(cls_ms, 2),
+            "routed_ms_per_denoise_step": round(ms, 3), "routed_ms_per_layer": round(ms / len(layers), 4)}
+
+
 def cpu_baseline(inp, rows_per_head):
     """The oracle as it stands, on a sample of query rows of every head; scaled to
     ms per layer-step by the fraction of rows computed."""
@@ -267,6 +331,11 @@ def main():
                                          (sec["routed"]["kernels"]["dense"][0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "classify_ms": round(sec["classify_ms"], 3)}
         del sec
+    print("[bench] table-4 style ablation", file=sys.stderr, flush=True)
+    out["ablation_720p"] = ablation(main_res, max(3, a.steps // 2), 2)
+    if a.full_step:
+        print("[bench] 30-layer step with classification", file=sys.stderr, flush=True)
+        out["full_step"] = full_step(max(3, a.steps // 4), 2)
     if not a.no_cpu:
         print("[bench] cpu oracle sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(main_res["inp"], a.cpu_rows)

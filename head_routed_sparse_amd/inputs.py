@@ -188,3 +188,54 @@ def full_step_layer_inputs(name: str, layer: int, geom: Optional[Geometry] = Non
     labels = full_step_labels(name)[layer]
     rng = np.random.Generator(np.random.PCG64([cfg["seed"], layer + 1]))
     return generate(geom, labels, cfg["seed"], None, True, rng=rng)
+
+
+def generate_torch(geom: Geometry, labels, seed: int, device="cuda", planted: bool = False,
+                   n_hist_frames: Optional[int] = None):
+    """The recipe of `generate` drawn with torch's generator on `device` (fast at full
+    size; different numbers from the numpy path). Returns a dict of tensors in the
+    geometry's dtype plus the labels. Used where the truth is the planted labels."""
+    import torch
+    if n_hist_frames is None:
+        n_hist_frames = geom.hist_frames
+    S, C, H, d = geom.tokens_per_frame, geom.chunk_frames, geom.num_heads, geom.head_dim
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    kw = dict(generator=g, device=device, dtype=torch.float32)
+    q = torch.randn((C * S, H, d), **kw)
+    k_hist = torch.randn((n_hist_frames * S, H, d), **kw)
+    v_hist = torch.randn((n_hist_frames * S, H, d), **kw)
+    k_cur = torch.randn((C * S, H, d), **kw)
+    v_cur = torch.randn((C * S, H, d), **kw)
+    labels = np.asarray(labels, dtype=np.int32)
+    if planted:
+        def direction(n, boost):
+            v = torch.randn((n, d), **kw)
+            return v / v.norm(dim=1, keepdim=True) * float(np.sqrt(boost * np.sqrt(d)))
+        for h in range(H):
+            cls = int(labels[h])
+            if cls in (SINK, DUMMY):
+                u = direction(1, PLANT_BOOST_BLOCK)[0]
+                q[:, h] += u
+                if cls == SINK:
+                    k_hist[: C * S, h] += u
+                else:
+                    k_cur[:, h] += u
+            elif cls == SPATIAL:
+                b = direction(S, PLANT_BOOST_SPATIAL)
+                q[:, h] += b.repeat(C, 1)
+                k_hist[:, h] += b.repeat(n_hist_frames, 1)
+                k_cur[:, h] += b.repeat(C, 1)
+    dt = torch.bfloat16 if geom.dtype == "bf16" else torch.float32
+    out = {k: v.to(dt) for k, v in dict(q=q, k_hist=k_hist, v_hist=v_hist, k_cur=k_cur, v_cur=v_cur).items()}
+    out["labels"] = labels
+    out["n_hist_frames"] = n_hist_frames
+    return out
+
+
+def full_step_layer_torch(name: str, layer: int, device="cuda"):
+    """Planted inputs of one layer of a multi-layer configuration, drawn on the device
+    from seed (seed * 1000 + layer + 1); labels from `full_step_labels`."""
+    cfg = CONFIGS[name]
+    return generate_torch(cfg["geom"], full_step_labels(name)[layer], cfg["seed"] * 1000 + layer + 1,
+                          device, planted=True)

@@ -40,3 +40,16 @@ def assert_close(got, want, max_abs, mean_abs, what=""):
 
 
 TOL = {"bf16": (1e-2, 1e-3), "f32": (1e-4, 1e-5)}
+
+
+def assert_close_bf16_storage(got, want, what=""):
+    """The bf16 tolerance plus the output's own storage rounding: an output of magnitude
+    |o| is stored with a half-ulp of up to 2^-8 |o|, which exceeds 1e-2 by itself once
+    |o| > 2.56 (planted heads concentrate attention on a few keys and reach |o| ~ 4)."""
+    err = np.abs(got - want)
+    mag = np.abs(want)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    bad = err > 1e-2 + 2.0 ** -8 * mag
+    assert not bad.any(), f"{what}: {bad.sum()} elements beyond 1e-2 + 2^-8|o| (max err {err.max():.3e})"
+    assert err.mean() <= 1e-3 + 2.0 ** -9 * mag.mean(), f"{what}: mean-abs {err.mean():.3e}"
+    return float(err.max()), float(err.mean()), float(mag.max())
