@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=2048, help="query rows per head in the CPU sample")
     ap.add_argument("--no-full-step", dest="full_step", action="store_false",
                     help="skip the 30-layer planted step")
+    ap.add_argument("--labels", default="", choices=["", "global"],
+                    help="profiling runs: 'global' times the full-window call instead of the routed one")
     ap.add_argument("--only-routed", action="store_true",
                     help="profiling runs: time only the routed call of the main workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -100,7 +102,7 @@ def time_calls(fn, steps, warmup):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
-def measure(name, steps, warmup, with_events, only_routed=False):
+def measure(name, steps, warmup, with_events, only_routed=False, labels_override=""):
     import torch
     from head_routed_sparse_amd import headcast as hc
     from head_routed_sparse_amd import inputs as hin
@@ -113,7 +115,7 @@ def measure(name, steps, warmup, with_events, only_routed=False):
     q, kh, vh, kc, vc = (dev(a) for a in (inp.q, inp.k_hist, inp.v_hist, inp.k_cur, inp.v_cur))
     desc = hc.make_desc(g)
     res = {}
-    runs = [("routed", inp.labels)]
+    runs = [("routed", np.full(g.num_heads, 3, np.int32) if labels_override == "global" else inp.labels)]
     if not only_routed:
         runs.append(("all_global", np.full(g.num_heads, 3, np.int32)))
     for tag, labels in runs:
@@ -266,7 +268,8 @@ def main():
         torch.cuda.synchronize()
         print(f"[bench] copy calibration: {n} bytes read, {n} bytes written", file=sys.stderr, flush=True)
         del src, dst
-    main_res = measure(a.config, a.steps, a.warmup, with_events=True, only_routed=a.only_routed)
+    main_res = measure(a.config, a.steps, a.warmup, with_events=True, only_routed=a.only_routed,
+                       labels_override=a.labels)
     g = main_res["geom"]
     if a.only_routed:
         r = main_res["routed"]
