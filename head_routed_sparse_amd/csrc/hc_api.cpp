@@ -72,6 +72,8 @@ hc_status check_desc(const hc_layer_desc* d) {
     return fail(HC_ERR_SHAPE, "window_frames %d must be a positive multiple of chunk_frames %d",
                 d->window_frames, d->chunk_frames);
   if (d->grid_h < 1 || d->grid_w < 1) return fail(HC_ERR_SHAPE, "grid %dx%d must be >= 1", d->grid_h, d->grid_w);
+  if (d->variant < 0 || d->variant > (HC_VARIANT_DUMMY_PREVIOUS | HC_VARIANT_SPATIAL_CELLS))
+    return fail(HC_ERR_SHAPE, "variant %d unknown", d->variant);
   if (!(d->softmax_scale > 0.f) || !std::isfinite(d->softmax_scale))
     return fail(HC_ERR_SHAPE, "softmax_scale must be positive and finite");
   const int64_t keys = (int64_t)d->window_frames * tokens_per_frame(*d);
@@ -284,11 +286,14 @@ struct hc_head_buffers {
 
 namespace {
 
+bool dummy_prev(const hc_layer_desc& d) { return (d.variant & HC_VARIANT_DUMMY_PREVIOUS) != 0; }
+bool spatial_cells(const hc_layer_desc& d) { return (d.variant & HC_VARIANT_SPATIAL_CELLS) != 0; }
+
 int64_t capacity_rows(const hc_layer_desc& d, int cls) {
   const int64_t S = tokens_per_frame(d);
   if (d.window_frames == d.chunk_frames) return 0;
   if (cls == HC_SINK) return (int64_t)d.chunk_frames * S;
-  if (cls == HC_DUMMY) return 0;
+  if (cls == HC_DUMMY) return dummy_prev(d) ? (int64_t)d.chunk_frames * S : 0;
   return (int64_t)(d.window_frames - d.chunk_frames) * S;
 }
 
@@ -305,7 +310,8 @@ size_t layout(const hc_layer_desc& d, const int32_t* labels, std::vector<int64_t
 
 // History frames currently stored for a head class, given the next block index.
 int64_t stored_frames(const hc_layer_desc& d, int cls, int64_t next_block) {
-  if (d.window_frames == d.chunk_frames || next_block <= 0 || cls == HC_DUMMY) return 0;
+  if (d.window_frames == d.chunk_frames || next_block <= 0) return 0;
+  if (cls == HC_DUMMY) return dummy_prev(d) ? d.chunk_frames : 0;   // the window's latest history block
   if (cls == HC_SINK) return d.chunk_frames;
   const int64_t rolling = std::min<int64_t>(next_block - 1, rolling_blocks(d));
   return (1 + rolling) * d.chunk_frames;
@@ -325,7 +331,8 @@ void build_plan(hc_head_buffers* b) {
       e.cur_len = lq;
       e.slot = -1;
       e.hist_off = b->head_off[h] < 0 ? 0 : b->head_off[h];
-      if (cls == HC_SINK || cls == HC_GLOBAL) e.hist_len = (int)(stored_frames(d, cls, next_block) * S);
+      if (cls == HC_SPATIAL && spatial_cells(d)) continue;   // served whole by the cell kernel
+      if (cls != HC_SPATIAL) e.hist_len = (int)(stored_frames(d, cls, next_block) * S);
       es.push_back(e);
     }
     plan_splits(es, nqt);
@@ -336,6 +343,16 @@ void build_plan(hc_head_buffers* b) {
   int slot = 0;
   b->merges.clear();
   b->spatials.clear();
+  if (spatial_cells(d))
+    for (int h = 0; h < d.num_heads; ++h)
+      if (b->labels[h] == HC_SPATIAL) {
+        SpatialEntry se{};
+        se.hist_off = b->head_off[h] < 0 ? 0 : b->head_off[h];
+        se.head = h;
+        se.cur_slot = -1;
+        se.out_slot = -1;
+        b->spatials.push_back(se);
+      }
   for (Entry& e : es) {
     const int cls = b->labels[e.head];
     if (cls == HC_SPATIAL) {
@@ -362,7 +379,7 @@ void build_plan(hc_head_buffers* b) {
   int ms = 0;
   for (const Entry& e : full) {
     const int cls = b->labels[e.head];
-    ms += cls == HC_SPATIAL ? 1 : (e.nsplit > 1 ? e.nsplit : 0);
+    ms += (cls == HC_SPATIAL && !spatial_cells(d)) ? 1 : (e.nsplit > 1 ? e.nsplit : 0);
   }
   b->max_slots = std::max(ms, slot);
 }
@@ -442,8 +459,9 @@ hc_status hc_build_head_buffers(const hc_layer_desc* desc, const int32_t* labels
   const size_t es_ = esize(d);
   hipStream_t s = (hipStream_t)stream;
   // Build: the stored frames are a prefix of the logical history (block b <= R sits at
-  // position b), so each head copies one contiguous row range.
-  for (int pass = 0; pass < 2 && n_hist_frames > 0; ++pass) {
+  // position b), so each head copies one contiguous row range; a Dummy head with a
+  // buffer copies the history's last block.
+  for (int pass = 0; pass < 3 && n_hist_frames > 0; ++pass) {
     CopyParams p{};
     p.src_k = k_hist;
     p.src_v = v_hist;
@@ -451,16 +469,18 @@ hc_status hc_build_head_buffers(const hc_layer_desc* desc, const int32_t* labels
     p.dst_v = b->mem + b->v_region;
     p.src_stride = (int64_t)d.num_heads * d.head_dim * es_;
     p.row_bytes = d.head_dim * (int)es_;
+    const int want = pass == 0 ? HC_SINK : (pass == 1 ? HC_GLOBAL : HC_DUMMY);
+    const int64_t first_row = pass == 2 ? (int64_t)(n_hist_frames - d.chunk_frames) * S : 0;
     int n = 0;
     for (int h = 0; h < d.num_heads; ++h) {
-      const int cls = b->labels[h];
-      if (b->head_off[h] < 0 || (pass == 0) != (cls == HC_SINK)) continue;
-      p.e[n].src_off = (int64_t)h * d.head_dim * es_;
+      const int cls = b->labels[h] == HC_SPATIAL ? HC_GLOBAL : b->labels[h];
+      if (b->head_off[h] < 0 || cls != want) continue;
+      p.e[n].src_off = ((int64_t)h * d.head_dim + first_row * d.num_heads * d.head_dim) * (int64_t)es_;
       p.e[n].dst_off = b->head_off[h] * (int64_t)es_;
       ++n;
     }
     p.n_entries = n;
-    p.rows = (int)(stored_frames(d, pass == 0 ? HC_SINK : HC_GLOBAL, b->next_block) * S);
+    p.rows = (int)(stored_frames(d, want, b->next_block) * S);
     if (n) {
       hipError_t e = timed(K_COPY, s, [&] { return launch_copy(p, s); });
       if (e != hipSuccess) {
@@ -518,8 +538,12 @@ hc_status hc_append_chunk(hc_head_buffers* b, const void* k_chunk, const void* v
       const int cls = b->labels[h];
       if (b->head_off[h] < 0) continue;
       if (cls == HC_SINK && pos != 0) continue;
+      // a Dummy buffer holds the window's latest history block: every new block while
+      // rolling blocks exist, else only the sink block
+      if (cls == HC_DUMMY && !(blk == 0 || R > 0)) continue;
+      const int64_t at = cls == HC_DUMMY ? 0 : pos;
       p.e[n].src_off = (int64_t)h * d.head_dim * es_;
-      p.e[n].dst_off = (b->head_off[h] + (int64_t)pos * d.chunk_frames * S * d.head_dim) * (int64_t)es_;
+      p.e[n].dst_off = (b->head_off[h] + at * d.chunk_frames * S * d.head_dim) * (int64_t)es_;
       ++n;
     }
     p.n_entries = n;
@@ -614,6 +638,9 @@ hc_status hc_routed_attention(const hc_head_buffers* b, const void* q, const voi
     sp.tiles_r = ceil_div(d.frame_h, kSpTileR);
     sp.tiles_c = ceil_div(d.frame_w, kSpTileC);
     sp.scale_log2 = p.scale_log2;
+    sp.cells = spatial_cells(d) ? 1 : 0;
+    sp.k_cur = k_cur;
+    sp.v_cur = v_cur;
     sp.n_entries = (int)b->spatials.size();
     for (size_t i = 0; i < b->spatials.size(); ++i) sp.e[i] = b->spatials[i];
     HC_HIP(timed(bf16 ? K_SPATIAL : K_F32, s, [&] { return launch_spatial(sp, d.head_dim, bf16, s); }));
@@ -832,7 +859,13 @@ hc_status hc_debug_slot_table(const hc_head_buffers* b, int32_t* frames) {
     int32_t* row = frames + (size_t)h * HF;
     for (int i = 0; i < HF; ++i) row[i] = -1;
     const int cls = b->labels[h];
-    if (cls == HC_DUMMY || HF == 0 || b->next_block <= 0) continue;
+    if (HF == 0 || b->next_block <= 0) continue;
+    if (cls == HC_DUMMY) {
+      if (!dummy_prev(d)) continue;
+      const int64_t blk = R > 0 ? b->next_block - 1 : 0;   // the window's latest history block
+      for (int i = 0; i < C; ++i) row[i] = (int32_t)(blk * C + i);
+      continue;
+    }
     for (int i = 0; i < C; ++i) row[i] = i;   // sink block (absolute block 0)
     if (cls == HC_SINK || R == 0) continue;
     // the latest block stored at each rolling position
@@ -866,7 +899,9 @@ hc_status hc_debug_gather_origins(const hc_layer_desc* desc, int32_t grid_h, int
   HC_TRY(check_ptr(r0c0, "r0c0"));
   if (grid_h < 1 || grid_w < 1) return fail(HC_ERR_SHAPE, "grid must be >= 1");
   HC_TRY(check_device());
-  HC_HIP(launch_gather_origins(desc->frame_h, desc->frame_w, grid_h, grid_w, (int32_t*)r0c0, (hipStream_t)stream));
+  HC_HIP(launch_gather_origins(desc->frame_h, desc->frame_w, grid_h, grid_w,
+                              (desc->variant & HC_VARIANT_SPATIAL_CELLS) ? 1 : 0, (int32_t*)r0c0,
+                              (hipStream_t)stream));
   return ok();
 }
 

@@ -202,8 +202,12 @@ __global__ __launch_bounds__(64) void spatial_attn_f32(const SpatialParams p) {
   const int pos = blockIdx.x * 64 + threadIdx.x;
   if (pos >= S) return;
   const int r = pos / fw, c = pos % fw;
-  const int r0 = win_origin(r, p.grid_h, fh), c0 = win_origin(c, p.grid_w, fw);
-  const int eh = min(p.grid_h, fh), ew = min(p.grid_w, fw);
+  const bool cells = p.cells != 0;
+  const int r0 = cells ? cell_origin(r, p.grid_h) : win_origin(r, p.grid_h, fh);
+  const int c0 = cells ? cell_origin(c, p.grid_w) : win_origin(c, p.grid_w, fw);
+  const int eh = cells ? cell_extent(r, p.grid_h, fh) : min(p.grid_h, fh);
+  const int ew = cells ? cell_extent(c, p.grid_w, fw) : min(p.grid_w, fw);
+  const int n_frames = p.n_hist_frames + (cells ? p.chunk_frames : 0);
   for (int cf = 0; cf < p.chunk_frames; ++cf) {
     const int q_row = cf * S + pos;
     const float* qp = (const float*)p.q + (int64_t)q_row * p.tok_stride + (int64_t)e.head * D;
@@ -213,12 +217,20 @@ __global__ __launch_bounds__(64) void spatial_attn_f32(const SpatialParams p) {
       o[d] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
-    for (int f = 0; f < p.n_hist_frames; ++f)
+    for (int f = 0; f < n_frames; ++f)
       for (int kr = r0; kr < r0 + eh; ++kr)
         for (int kc = c0; kc < c0 + ew; ++kc) {
-          const int64_t row = (int64_t)f * S + kr * fw + kc;
-          const float* kp = (const float*)p.k_hist + e.hist_off + row * p.hist_stride;
-          const float* vp = (const float*)p.v_hist + e.hist_off + row * p.hist_stride;
+          const float* kp;
+          const float* vp;
+          if (f < p.n_hist_frames) {
+            const int64_t row = (int64_t)f * S + kr * fw + kc;
+            kp = (const float*)p.k_hist + e.hist_off + row * p.hist_stride;
+            vp = (const float*)p.v_hist + e.hist_off + row * p.hist_stride;
+          } else {
+            const int64_t tok = (int64_t)(f - p.n_hist_frames) * S + kr * fw + kc;
+            kp = (const float*)p.k_cur + tok * p.tok_stride + (int64_t)e.head * D;
+            vp = (const float*)p.v_cur + tok * p.tok_stride + (int64_t)e.head * D;
+          }
           float s = 0.f;
           for (int d = 0; d < D; ++d) s += qv[d] * kp[d];
           s *= p.scale_log2;
@@ -229,7 +241,10 @@ __global__ __launch_bounds__(64) void spatial_attn_f32(const SpatialParams p) {
           for (int d = 0; d < D; ++d) o[d] = o[d] * fct + w * vp[d];
           m = mn;
         }
-    if (e.out_slot >= 0) {
+    float* op = (float*)p.out + (int64_t)q_row * p.tok_stride + (int64_t)e.head * D;
+    if (cells) {
+      for (int d = 0; d < D; ++d) op[d] = o[d] / l;
+    } else if (e.out_slot >= 0) {
       const int64_t prow = (int64_t)e.out_slot * p.lq + q_row;
       for (int d = 0; d < D; ++d) p.part_o[prow * D + d] = o[d];
       p.part_ml[prow * 2] = m;
@@ -241,7 +256,6 @@ __global__ __launch_bounds__(64) void spatial_attn_f32(const SpatialParams p) {
       const float wa = m == -INFINITY ? 0.f : exp2f(m - M);
       const float wc = exp2f(m_c - M);
       const float inv = 1.0f / (wa * l + wc * l_c);
-      float* op = (float*)p.out + (int64_t)q_row * p.tok_stride + (int64_t)e.head * D;
       for (int d = 0; d < D; ++d) op[d] = (wa * o[d] + wc * p.part_o[crow * D + d]) * inv;
     }
   }

@@ -96,7 +96,10 @@ struct SpatialParams {
   int32_t tiles_r, tiles_c;  // position tiles per frame
   int32_t n_entries;
   float scale_log2;
-  int32_t pad;
+  int32_t cells;           // 1: own non-overlapping cell in every window frame (current
+                           //    block read from k_cur / v_cur), output written directly
+  const void* k_cur;       // [C*S][H][D], cell mode only
+  const void* v_cur;
   SpatialEntry e[kMaxEntries];
 };
 
@@ -146,7 +149,7 @@ hipError_t launch_merge(const MergeParams& p, int head_dim, int bf16, hipStream_
 hipError_t launch_spatial(const SpatialParams& p, int head_dim, int bf16, hipStream_t s);
 hipError_t launch_copy(const CopyParams& p, hipStream_t s);
 hipError_t launch_stats(const StatsParams& p, hipStream_t s);
-hipError_t launch_gather_origins(int frame_h, int frame_w, int grid_h, int grid_w, int32_t* out,
+hipError_t launch_gather_origins(int frame_h, int frame_w, int grid_h, int grid_w, int cells, int32_t* out,
                                  hipStream_t s);
 
 int dense_items_grid(int n_items, int xcd_group);   // workgroups for n_items (XCD-grouped padding)

@@ -70,6 +70,14 @@ __host__ __device__ __forceinline__ int win_origin(int pos, int g, int extent) {
   return o < 0 ? 0 : (o > hi ? hi : o);
 }
 
+// Non-overlapping cells: origin and size of the cell holding pos (the last cell keeps
+// the remainder rows / columns).
+__host__ __device__ __forceinline__ int cell_origin(int pos, int cell) { return (pos / cell) * cell; }
+__host__ __device__ __forceinline__ int cell_extent(int pos, int cell, int extent) {
+  const int o = cell_origin(pos, cell);
+  return cell < extent - o ? cell : extent - o;
+}
+
 // Work item -> logical index, keeping runs of kXcdGroup consecutive logical items on
 // one XCD (workgroups are dispatched round-robin over the 8 XCDs) while the overall
 // dispatch order still follows the logical order.

@@ -26,16 +26,23 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
   const SpatialEntry e = p.e[blockIdx.y];
   const int tr = blockIdx.x / p.tiles_c, tc = blockIdx.x % p.tiles_c;
   const int fh = p.frame_h, fw = p.frame_w, S = fh * fw;
-  const int eh = min(p.grid_h, fh), ew = min(p.grid_w, fw);
+  const bool cells = p.cells != 0;
+  // window of a position: sliding g x g (never cut) or its own cell
+  auto org_r = [&](int r) { return cells ? cell_origin(r, p.grid_h) : win_origin(r, p.grid_h, fh); };
+  auto org_c = [&](int c) { return cells ? cell_origin(c, p.grid_w) : win_origin(c, p.grid_w, fw); };
+  auto ext_r = [&](int r) { return cells ? cell_extent(r, p.grid_h, fh) : min(p.grid_h, fh); };
+  auto ext_c = [&](int c) { return cells ? cell_extent(c, p.grid_w, fw) : min(p.grid_w, fw); };
   const int R0 = tr * kSpTileR, C0 = tc * kSpTileC;
   const int R1 = min(R0 + kSpTileR, fh) - 1, C1 = min(C0 + kSpTileC, fw) - 1;
-  // union of the windows of the tile's positions
-  const int ur0 = win_origin(R0, p.grid_h, fh), ur1 = win_origin(R1, p.grid_h, fh) + eh;
-  const int uc0 = win_origin(C0, p.grid_w, fw), uc1 = win_origin(C1, p.grid_w, fw) + ew;
+  // union of the windows of the tile's positions (origins and ends grow with the position)
+  const int ur0 = org_r(R0), ur1 = org_r(R1) + ext_r(R1);
+  const int uc0 = org_c(C0), uc1 = org_c(C1) + ext_c(C1);
   const int UW = uc1 - uc0;
   const int nU = (ur1 - ur0) * UW;
   const int nchunk = (nU + kKeyTile - 1) / kKeyTile;
-  const int n_tiles = p.n_hist_frames * nchunk;
+  // frames walked: the history (and, for cells, the current block after it)
+  const int n_frames = p.n_hist_frames + (cells ? p.chunk_frames : 0);
+  const int n_tiles = n_frames * nchunk;
 
   const int tid = threadIdx.x;
   constexpr int nwave = 4;   // one wave per chunk frame; spare waves only load
@@ -45,23 +52,30 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
   const int half = lane >> 5;
   const int pr = R0 + l32 / kSpTileC, pc = C0 + l32 % kSpTileC;
   const bool pos_ok = pr < fh && pc < fw;
-  const int r0q = win_origin(min(pr, fh - 1), p.grid_h, fh);
-  const int c0q = win_origin(min(pc, fw - 1), p.grid_w, fw);
+  const int r0q = org_r(min(pr, fh - 1)), ehq = ext_r(min(pr, fh - 1));
+  const int c0q = org_c(min(pc, fw - 1)), ewq = ext_c(min(pc, fw - 1));
 
   const uint16_t* kh = (const uint16_t*)p.k_hist + e.hist_off;
   const uint16_t* vh = (const uint16_t*)p.v_hist + e.hist_off;
-  const int64_t hs = p.hist_stride;
+  const uint16_t* kcb = cells ? (const uint16_t*)p.k_cur + (int64_t)e.head * D : kh;
+  const uint16_t* vcb = cells ? (const uint16_t*)p.v_cur + (int64_t)e.head * D : vh;
+  const int64_t hs = p.hist_stride, ts = p.tok_stride;
+  const int nh = p.n_hist_frames;
 
   TileRegs<D> regs;
-  auto key_row = [&](int t, int j) -> int64_t {   // history row of local key j of tile t
+  // element offset of local key j of tile t: frame t / nchunk of the history, or of the
+  // current block (cell mode, frames nh..), at the union position of chunk t % nchunk
+  auto key_off = [&](int t, int j, bool& cur) -> int64_t {
     const int f = t / nchunk;
     const int ui = min((t - f * nchunk) * kKeyTile + j, nU - 1);
     const int kr = ur0 + ui / UW, kcol = uc0 + ui % UW;
-    return (int64_t)f * S + (int64_t)kr * fw + kcol;
+    cur = f >= nh;
+    const int64_t tok = (int64_t)(cur ? f - nh : f) * S + (int64_t)kr * fw + kcol;
+    return tok * (cur ? ts : hs);
   };
   auto load = [&](int t) {
-    load_tile<D>(regs, [&](int j) { return kh + key_row(t, j) * hs; },
-                 [&](int j) { return vh + key_row(t, j) * hs; }, tid);
+    load_tile<D>(regs, [&](int j) { bool c; const int64_t o = key_off(t, j, c); return (c ? kcb : kh) + o; },
+                 [&](int j) { bool c; const int64_t o = key_off(t, j, c); return (c ? vcb : vh) + o; }, tid);
   };
   auto store = [&](int t, int b) {
     if (tid < kKeyTile) {
@@ -108,7 +122,7 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
         const int kc2 = kr4[kb][r >> 2][r & 3];
         const unsigned dr = (unsigned)((kc2 >> 16) - r0q);
         const unsigned dc = (unsigned)((kc2 & 0xFFFF) - c0q);
-        return dr < (unsigned)eh && dc < (unsigned)ew;
+        return dr < (unsigned)ehq && dc < (unsigned)ewq;
       });
       if (more) store(t + 1, (t + 1) & 1);
       __syncthreads();
@@ -116,7 +130,10 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
 
     const float l_tot = sum_halves(st.l_run);
     if (q_ok) {
-      if (e.out_slot >= 0) {
+      if (cells) {   // the whole key set was walked here: normalise and write
+        uint16_t* op = (uint16_t*)p.out + (int64_t)q_row * p.tok_stride + (int64_t)e.head * D;
+        store_out_bf16<D>(st, 1.0f / l_tot, op, half);
+      } else if (e.out_slot >= 0) {
         const int64_t prow = (int64_t)e.out_slot * p.lq + q_row;
         store_partial<D>(st, l_tot, p.part_o + prow * D, p.part_ml + prow * 2, half);
       } else {
@@ -147,11 +164,11 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
   }
 }
 
-__global__ void gather_origins_kernel(int fh, int fw, int gh, int gw, int32_t* out) {
+__global__ void gather_origins_kernel(int fh, int fw, int gh, int gw, int cells, int32_t* out) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= fh * fw) return;
-  out[2 * t] = win_origin(t / fw, gh, fh);
-  out[2 * t + 1] = win_origin(t % fw, gw, fw);
+  out[2 * t] = cells ? cell_origin(t / fw, gh) : win_origin(t / fw, gh, fh);
+  out[2 * t + 1] = cells ? cell_origin(t % fw, gw) : win_origin(t % fw, gw, fw);
 }
 
 }  // namespace
@@ -169,11 +186,11 @@ hipError_t launch_spatial(const SpatialParams& p, int head_dim, int bf16, hipStr
   return hipGetLastError();
 }
 
-hipError_t launch_gather_origins(int frame_h, int frame_w, int grid_h, int grid_w, int32_t* out,
+hipError_t launch_gather_origins(int frame_h, int frame_w, int grid_h, int grid_w, int cells, int32_t* out,
                                  hipStream_t s) {
   const int n = frame_h * frame_w;
   hipLaunchKernelGGL(gather_origins_kernel, dim3((n + 255) / 256), dim3(256), 0, s, frame_h, frame_w,
-                     grid_h, grid_w, out);
+                     grid_h, grid_w, cells, out);
   return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libheadcast.so")
 
 SINK, DUMMY, SPATIAL, GLOBAL = 0, 1, 2, 3
 HC_BF16, HC_F32 = 0, 1
+HC_VARIANT_DUMMY_PREVIOUS, HC_VARIANT_SPATIAL_CELLS = 1, 2
 KERNEL_KINDS = ("dense", "merge", "spatial", "copy", "stats", "fp32")
 
 
@@ -30,7 +31,8 @@ class LayerDesc(ctypes.Structure):
                 ("frame_h", ctypes.c_int32), ("frame_w", ctypes.c_int32),
                 ("chunk_frames", ctypes.c_int32), ("window_frames", ctypes.c_int32),
                 ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("variant", ctypes.c_int32)]
 
 
 class ClassifyParams(ctypes.Structure):
@@ -110,11 +112,11 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def make_desc(geom) -> LayerDesc:
+def make_desc(geom, variant: int = 0) -> LayerDesc:
     """LayerDesc from an object with the Geometry fields (see inputs.Geometry)."""
     return LayerDesc(geom.num_heads, geom.head_dim, geom.frame_h, geom.frame_w,
                      geom.chunk_frames, geom.window_frames, geom.grid_h, geom.grid_w,
-                     float(geom.softmax_scale), HC_BF16 if geom.dtype == "bf16" else HC_F32)
+                     float(geom.softmax_scale), HC_BF16 if geom.dtype == "bf16" else HC_F32, int(variant))
 
 
 def hc_default_classify_params(**overrides) -> ClassifyParams:

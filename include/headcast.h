@@ -56,6 +56,18 @@ typedef enum {
 
 typedef enum { HC_BF16 = 0, HC_F32 = 1 } hc_dtype;
 
+/* Path variants (hc_layer_desc.variant, a bit set). The default (0) follows the
+ * classifier's proxies: Dummy = current block; Spatial = current block + the sliding
+ * grid_h x grid_w window in every history frame. The pages' deployed forms:
+ *  HC_VARIANT_DUMMY_PREVIOUS: Dummy heads also attend the window's most recent history
+ *    block (appendix B cost model; Sec. 4.4's fused Sink/Dummy launch over one block);
+ *    Dummy heads then keep a one-block buffer.
+ *  HC_VARIANT_SPATIAL_CELLS: Spatial heads attend only the keys of their own
+ *    non-overlapping grid_h x grid_w cell (cells tile the frame from (0,0); the last
+ *    row/column of cells keeps the remainder) in every window frame, the current block
+ *    included (Sec. 4.4, Fig. 3; Sec. 5.1 uses 10 x 10 cells). */
+typedef enum { HC_VARIANT_DUMMY_PREVIOUS = 1, HC_VARIANT_SPATIAL_CELLS = 2 } hc_variant;
+
 typedef struct {
   int32_t num_heads;      /* H, 1..64 */
   int32_t head_dim;       /* d, 64 or 128 */
@@ -67,6 +79,7 @@ typedef struct {
   int32_t grid_w;         /* Spatial path window columns */
   float softmax_scale;    /* usually 1/sqrt(d) */
   int32_t dtype;          /* hc_dtype */
+  int32_t variant;        /* hc_variant bits, 0 = proxy-consistent paths */
 } hc_layer_desc;
 
 /* Classifier parameters (Sec. 4.2 Eq. 5 thresholds; Eq. 4 gamma and percentile). */
@@ -90,7 +103,8 @@ hc_status hc_default_classify_params(hc_classify_params* params);
 
 /* ---------------------------------------------------------------- buffers (Sec. 4.3)
  * Per-head compact KV buffers split out of the monolithic cache: a Sink head keeps
- * the frozen first block (C*S rows); a Dummy head keeps nothing; Spatial and Global
+ * the frozen first block (C*S rows); a Dummy head keeps nothing (with
+ * HC_VARIANT_DUMMY_PREVIOUS: the window's latest history block, C*S rows); Spatial and Global
  * heads keep the sink block plus R = F/C - 2 rolling blocks ((F - C)*S rows), the
  * block with absolute index b >= 1 living at block position 1 + (b - 1) mod R.
  */

@@ -33,6 +33,10 @@ import numpy as np
 SINK, DUMMY, SPATIAL, GLOBAL = 0, 1, 2, 3
 COS_EPS = 1e-8
 
+# Path variants the pages also describe (deployed forms; see key_set_mask):
+DUMMY_PREVIOUS_BLOCK = 1   # Dummy heads also see the latest finished block
+SPATIAL_CELLS = 2          # Spatial heads see their own non-overlapping cell in every frame
+
 
 # ----------------------------------------------------------------------------- geometry
 def window_origin(pos: np.ndarray | int, g: int, extent: int):
@@ -47,6 +51,16 @@ def window_extent(g: int, extent: int) -> int:
     return min(g, extent)
 
 
+def cell_origin(pos, cell: int):
+    """First row (column) of the non-overlapping cell holding `pos`: cells tile the frame
+    from row (column) 0; the last one keeps the remainder rows (columns)."""
+    return (np.asarray(pos) // cell) * cell
+
+
+def cell_extent(pos, cell: int, extent: int):
+    return np.minimum(cell, extent - cell_origin(pos, cell))
+
+
 def key_coords(frame_h: int, frame_w: int, n_frames: int):
     """(frame, row, col) of every token of `n_frames` consecutive frames (frame-major,
     row-major inside a frame)."""
@@ -56,7 +70,7 @@ def key_coords(frame_h: int, frame_w: int, n_frames: int):
 
 
 def key_set_mask(cls: int, geom, n_hist: int, q_tokens: np.ndarray, grid=None,
-                 sink_proxy: bool = False, sink_proxy_includes_current: bool = False):
+                 sink_proxy: bool = False, sink_proxy_includes_current: bool = False, variant: int = 0):
     """Boolean mask [len(q_tokens)][(n_hist + C) * S] over the logical window
     [history frames 0..n_hist-1 ; current block], for one head class.
 
@@ -64,9 +78,13 @@ def key_set_mask(cls: int, geom, n_hist: int, q_tokens: np.ndarray, grid=None,
       SINK    : the sink block (history frames 0..C-1) + the current block;
                 with sink_proxy=True: the sink block alone (the classifier's proxy),
                 plus the current block if sink_proxy_includes_current.
-      DUMMY   : the current block only.
+      DUMMY   : the current block only; with variant DUMMY_PREVIOUS_BLOCK also the
+                latest finished block (the last C history frames; appendix B's cost
+                model and Sec. 4.4's fused Sink/Dummy launch).
       SPATIAL : the current block + in each history frame the g x g window around the
-                query's (row, col).
+                query's (row, col); with variant SPATIAL_CELLS instead the query's own
+                non-overlapping g_h x g_w cell in every window frame, current block
+                included (Sec. 4.4, Fig. 3).
       GLOBAL  : every window frame.
     """
     C, S = geom.chunk_frames, geom.tokens_per_frame
@@ -81,11 +99,18 @@ def key_set_mask(cls: int, geom, n_hist: int, q_tokens: np.ndarray, grid=None,
     if cls == GLOBAL:
         m = np.ones((nq, kf.size), dtype=bool)
     elif cls == DUMMY:
-        m = np.broadcast_to(is_cur, (nq, kf.size)).copy()
+        keys = is_cur.copy()
+        if variant & DUMMY_PREVIOUS_BLOCK:
+            keys |= is_hist & (kf >= n_hist - C)
+        m = np.broadcast_to(keys, (nq, kf.size)).copy()
     elif cls == SINK:
         sink_keys = is_hist & (kf < C)
         keys = sink_keys if (sink_proxy and not sink_proxy_includes_current) else (sink_keys | is_cur)
         m = np.broadcast_to(keys, (nq, kf.size)).copy()
+    elif cls == SPATIAL and (variant & SPATIAL_CELLS):
+        same_row_cell = (kr[None, :] // gh) == (qr[:, None] // gh)
+        same_col_cell = (kc[None, :] // gw) == (qc[:, None] // gw)
+        m = same_row_cell & same_col_cell
     elif cls == SPATIAL:
         r0 = window_origin(qr, gh, fh)[:, None]
         c0 = window_origin(qc, gw, fw)[:, None]
@@ -127,7 +152,7 @@ def head_window(q, k_hist, v_hist, k_cur, v_cur, h):
 
 
 def path_attention(inp, h, cls, rows=None, block=512, grid=None, sink_proxy=False,
-                   sink_proxy_includes_current=False):
+                   sink_proxy_includes_current=False, variant=0):
     """Output [len(rows)][d] of head h restricted to the key set of `cls`
     (processed in blocks of query rows to bound memory)."""
     g = inp.geom
@@ -138,12 +163,12 @@ def path_attention(inp, h, cls, rows=None, block=512, grid=None, sink_proxy=Fals
     out = np.empty((rows.size, g.head_dim))
     for b in range(0, rows.size, block):
         r = rows[b:b + block]
-        m = key_set_mask(cls, g, inp.n_hist_frames, r, grid, sink_proxy, sink_proxy_includes_current)
+        m = key_set_mask(cls, g, inp.n_hist_frames, r, grid, sink_proxy, sink_proxy_includes_current, variant)
         out[b:b + block], _ = masked_attention(qh[r], kh, vh, m, g.softmax_scale)
     return out
 
 
-def routed_attention(inp, labels=None, rows=None, heads=None):
+def routed_attention(inp, labels=None, rows=None, heads=None, variant=0):
     """The routed step (HeadCast Sec. 4.4): head h attends over the key set of its
     class; outputs concatenated back along heads. Returns [len(rows)][H][d] float64."""
     g = inp.geom
@@ -153,11 +178,11 @@ def routed_attention(inp, labels=None, rows=None, heads=None):
     heads = range(g.num_heads) if heads is None else heads
     out = np.zeros((len(rows), g.num_heads, g.head_dim))
     for h in heads:
-        out[:, h, :] = path_attention(inp, h, int(labels[h]), rows)
+        out[:, h, :] = path_attention(inp, h, int(labels[h]), rows, variant=variant)
     return out
 
 
-def brute_force_attention(inp, h, cls, t, grid=None, sink_proxy=False):
+def brute_force_attention(inp, h, cls, t, grid=None, sink_proxy=False, variant=0):
     """One query token t of head h by a scalar loop: walk every window key, keep it if
     the class admits it (membership written out key by key), softmax in float64."""
     g = inp.geom
@@ -177,7 +202,9 @@ def brute_force_attention(inp, h, cls, t, grid=None, sink_proxy=False):
                 if cls == GLOBAL:
                     keep = True
                 elif cls == DUMMY:
-                    keep = current
+                    keep = current or (bool(variant & DUMMY_PREVIOUS_BLOCK) and n_hist - C <= f)
+                elif cls == SPATIAL and variant & SPATIAL_CELLS:
+                    keep = r // gh == qr // gh and c // gw == qc // gw
                 elif cls == SINK:
                     keep = (f < C and not current) or (current and not sink_proxy)
                 else:
@@ -289,16 +316,22 @@ def buffer_position_of_block(b: int, window_frames: int, chunk_frames: int):
     return 1 + (b - 1) % R
 
 
-def slot_table(labels, window_frames, chunk_frames, n_blocks_seen):
+def slot_table(labels, window_frames, chunk_frames, n_blocks_seen, variant=0):
     """Absolute frame held at every history frame position [H][F - C] (-1 = empty) after
     blocks 0..n_blocks_seen-1 were stored in order. Sink heads hold only the frozen
-    first block; Dummy heads hold nothing; Global/Spatial heads hold the ring."""
+    first block; Dummy heads hold nothing (with DUMMY_PREVIOUS_BLOCK: the window's most
+    recent history block, overwritten by every new one while rolling blocks exist);
+    Global/Spatial heads hold the ring."""
     C, F = chunk_frames, window_frames
     H = len(labels)
     table = -np.ones((H, F - C), dtype=np.int32)
     for h in range(H):
         cls = int(labels[h])
         if cls == DUMMY:
+            hist = window_history_blocks(n_blocks_seen, F, C)
+            if variant & DUMMY_PREVIOUS_BLOCK and hist:
+                b = hist[-1]                     # the window's most recent history block
+                table[h, :C] = np.arange(b * C, b * C + C)
             continue
         for b in range(n_blocks_seen):
             pos = buffer_position_of_block(b, F, C)

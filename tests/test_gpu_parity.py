@@ -4,6 +4,7 @@ Bit-exact: buffer contents, slot tables, Spatial window origins, labels.
 Floating point (outputs against the oracle on the same bf16-rounded inputs):
 max-abs <= 1e-2 and mean-abs <= 1e-3 for bf16; max-abs <= 1e-4 for fp32 inputs.
 """
+import dataclasses
 import zlib
 
 import numpy as np
@@ -251,3 +252,77 @@ def test_classify_sink_proxy_variant():
     got, _ = classify_gpu(inp, gamma=0.5, sink_proxy_includes_current=1)
     want, _ = orc.classify_heads(inp, dict(gamma=0.5, sink_proxy_includes_current=True))
     assert list(got) == list(want) == [S_, G_]
+
+
+# ----------------------------------------------------------------------------- path variants
+VARIANT_GEOMS = {
+    "10x13_C2_F8_d128_cells3": hin.Geometry(4, 128, 10, 13, 2, 8, 3, 3, "bf16"),
+    "9x17_C3_F12_d64_cells4x5": hin.Geometry(4, 64, 9, 17, 3, 12, 4, 5, "bf16"),
+    "12x20_C3_F9_d128_cells10": hin.Geometry(4, 128, 12, 20, 3, 9, 10, 10, "bf16"),
+    "tiny_f32_cells3": hin.CONFIGS["tiny"]["geom"],
+}
+
+
+@pytest.mark.parametrize("gname", list(VARIANT_GEOMS))
+@pytest.mark.parametrize("variant", [1, 2, 3])
+def test_variants_match_oracle(gname, variant):
+    g = VARIANT_GEOMS[gname]
+    inp = hin.generate(g, (S_, D_, P_, G_), seed=zlib.crc32(gname.encode()) % 1000 + variant)
+    t = to_device(inp)
+    buf = hc.hc_build_head_buffers(hc.make_desc(g, variant), inp.labels, t["k_hist"], t["v_hist"],
+                                   inp.n_hist_frames)
+    got = host(hc.hc_routed_attention(buf, t["q"], t["k_cur"], t["v_cur"]))
+    want = orc.routed_attention(inp, variant=variant)
+    print(gname, variant, assert_close(got, want, *TOL[g.dtype], what=f"{gname} v{variant}"))
+
+
+def test_variant_cell_origins_bit_exact():
+    for fh, fw, ch, cw in [(45, 80, 10, 10), (68, 120, 10, 10), (30, 52, 10, 10), (9, 17, 4, 5), (7, 7, 9, 9)]:
+        d = hc.make_desc(hin.Geometry(1, 64, fh, fw, 1, 2, ch, cw, "bf16"), hc.HC_VARIANT_SPATIAL_CELLS)
+        got = hc.hc_debug_gather_origins(d, ch, cw).cpu().numpy()
+        pos = np.arange(fh * fw)
+        want = np.stack([orc.cell_origin(pos // fw, ch), orc.cell_origin(pos % fw, cw)], axis=1)
+        assert np.array_equal(got, want), (fh, fw, ch, cw)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_variant_rollout_dummy_buffer(dtype):
+    """Warm-up with appends under both variants: the Dummy buffer always holds the
+    window's latest history block, bit-exact, and outputs follow the oracle."""
+    variant = 3
+    g = hin.Geometry(4, 64, 5, 9, 2, 8, 3, 3, dtype)
+    labels = (S_, D_, P_, G_)
+    C, S, H, d = g.chunk_frames, g.tokens_per_frame, g.num_heads, g.head_dim
+    rng = np.random.default_rng(9)
+    blocks = [hin.round_to_bf16(rng.standard_normal((3, C * S, H, d), dtype=np.float32)) for _ in range(7)]
+    buf = hc.hc_build_head_buffers(hc.make_desc(g, variant), labels, None, None, 0)
+    ws = hc.routed_workspace(buf)
+    for step in range(7):
+        q, k, v = blocks[step]
+        out = host(hc.hc_routed_attention(buf, dev(q, dtype), dev(k, dtype), dev(v, dtype), workspace=ws))
+        hist = orc.window_history_blocks(step, g.window_frames, C)
+        kh = np.concatenate([blocks[b][1] for b in hist]) if hist else np.zeros((0, H, d), np.float32)
+        vh = np.concatenate([blocks[b][2] for b in hist]) if hist else np.zeros((0, H, d), np.float32)
+        inp = hin.LayerInputs(g, np.array(labels, np.int32), q, kh, vh, k, v, len(hist) * C)
+        assert_close(out, orc.routed_attention(inp, variant=variant), *TOL[dtype], what=f"step {step}")
+        table = orc.slot_table(labels, g.window_frames, C, step, variant=orc.DUMMY_PREVIOUS_BLOCK)
+        assert np.array_equal(hc.hc_debug_slot_table(buf), table)
+        rows = buffer_rows(buf, 1, "k")
+        if table[1, 0] >= 0:
+            b = int(table[1, 0]) // C
+            assert np.array_equal(rows, blocks[b][1][:, 1, :].astype(np.float64))
+        hc.hc_append_chunk(buf, dev(k, dtype), dev(v, dtype))
+
+
+def test_variant_full_size_720p_sampled_rows():
+    """The pages' deployed paths at 720P: 10 x 10 cells for the Spatial heads and the
+    previous block for the Dummy heads."""
+    inp = hin.config_inputs("720p")
+    g = dataclasses.replace(inp.geom, grid_h=10, grid_w=10)
+    inp = dataclasses.replace(inp, geom=g)
+    t = to_device(inp)
+    buf = hc.hc_build_head_buffers(hc.make_desc(g, 3), inp.labels, t["k_hist"], t["v_hist"], inp.n_hist_frames)
+    out = host(hc.hc_routed_attention(buf, t["q"], t["k_cur"], t["v_cur"]))
+    rows = sample_rows(g, n_random=96, seed=2)
+    want = orc.routed_attention(inp, rows=rows, variant=3)
+    print(assert_close(out[rows], want, *TOL["bf16"], what="720p deployed variants"))

@@ -172,3 +172,34 @@ def test_reduce_statistics_and_decision_match_oracle():
                     assert hc.hc_decide(a, b, c, s, p) == orc.decide(
                         a, b, c, s, float(np.float32(0.95)), float(np.float32(0.95)),
                         float(np.float32(0.95)), float(np.float32(0.755)))
+
+
+@pytest.mark.parametrize("F,C", [(21, 3), (5, 1), (6, 3), (3, 3), (12, 2)])
+def test_variant_slot_table_matches_oracle(F, C):
+    g = hin.Geometry(4, 64, 3, 5, C, F, 2, 2, "bf16")
+    labels = [0, 1, 2, 3]
+    for n in range(0, 14):
+        pb = hc.hc_plan_head_buffers(hc.make_desc(g, hc.HC_VARIANT_DUMMY_PREVIOUS), labels, n)
+        assert np.array_equal(hc.hc_debug_slot_table(pb),
+                              orc.slot_table(labels, F, C, n, variant=orc.DUMMY_PREVIOUS_BLOCK)), n
+
+
+def test_variant_plans():
+    cfg = hin.CONFIGS["720p"]
+    g = cfg["geom"]
+    S = g.tokens_per_frame
+    for var in (1, 2, 3):
+        pb = hc.hc_plan_head_buffers(hc.make_desc(g, var), cfg["labels"], 7)
+        ents, _ = hc.hc_debug_routed_plan(pb)
+        heads = {int(r[0]): r for r in ents}
+        for h, cls in enumerate(cfg["labels"]):
+            if cls == 2 and var & 2:
+                assert h not in heads                       # whole key set in the cell kernel
+                continue
+            if cls == 1:
+                assert heads[h][1] == (g.chunk_frames * S if var & 1 else 0)
+        n = hc.hc_head_buffers_bytes(hc.make_desc(g, var), cfg["labels"])
+        base = hc.hc_head_buffers_bytes(hc.make_desc(g, 0), cfg["labels"])
+        assert n - base == (2 * 3 * g.chunk_frames * S * g.head_dim * 2 if var & 1 else 0)
+    with pytest.raises(hc.HCError):
+        hc.hc_head_buffers_bytes(hc.make_desc(g, 4), cfg["labels"])

@@ -352,3 +352,88 @@ def test_pages_flop_model_ratio():
     n = {c: orc.key_set_mask(c, geom, geom.hist_frames, rows).sum() for c in (S_, D_, G_)}
     assert n[S_] * 4 == n[G_]
     assert n[D_] * 8 == n[G_]
+
+
+# ----------------------------------------------------------------------------- variants
+V_DPREV, V_CELLS = orc.DUMMY_PREVIOUS_BLOCK, orc.SPATIAL_CELLS
+
+
+@pytest.mark.parametrize("g", [1, 2, 3, 4, 8])
+def test_variants_brute_force(g):
+    geom = small_geom(fh=5, fw=7, C=2, F=8, g=g)
+    inp = small_inputs(geom)
+    for cls, var in ((D_, V_DPREV), (P_, V_CELLS), (P_, V_CELLS | V_DPREV)):
+        dense = orc.path_attention(inp, 2, cls, variant=var)
+        for t in range(geom.lq):
+            bf = orc.brute_force_attention(inp, 2, cls, t, variant=var)
+            assert np.max(np.abs(bf - dense[t])) < 1e-12, (cls, var, t)
+
+
+def test_variant_special_cases():
+    # one cell covering the frame: Spatial cells = Global
+    geom = small_geom(fh=5, fw=7, C=2, F=8, g=7)
+    inp = small_inputs(geom)
+    assert np.allclose(orc.path_attention(inp, 1, P_, variant=V_CELLS), orc.path_attention(inp, 1, G_),
+                       atol=1e-14, rtol=0)
+    # window = sink block + current block: the previous block is the sink block
+    geom = small_geom(fh=5, fw=7, C=2, F=4)
+    inp = small_inputs(geom)
+    assert np.allclose(orc.path_attention(inp, 1, D_, variant=V_DPREV), orc.path_attention(inp, 1, S_),
+                       atol=1e-14, rtol=0)
+    # 1x1 cells: every query sees exactly its own position in each window frame
+    geom = small_geom(fh=5, fw=7, C=2, F=8, g=1)
+    rows = np.arange(geom.lq)
+    m = orc.key_set_mask(P_, geom, geom.hist_frames, rows, variant=V_CELLS)
+    assert np.all(m.sum(axis=1) == geom.window_frames)
+    kf, kr, kc = orc.key_coords(geom.frame_h, geom.frame_w, geom.window_frames)
+    S = geom.tokens_per_frame
+    for t in (0, 13, geom.lq - 1):
+        assert np.all(kr[m[t]] == (t % S) // geom.frame_w) and np.all(kc[m[t]] == t % geom.frame_w)
+
+
+def test_variant_cell_geometry_hand_values():
+    # 45-row frame, 10-row cells: four full cells and a 5-row remainder cell
+    assert [int(orc.cell_origin(r, 10)) for r in (0, 9, 10, 39, 40, 44)] == [0, 0, 10, 30, 40, 40]
+    assert [int(orc.cell_extent(r, 10, 45)) for r in (0, 39, 40, 44)] == [10, 10, 5, 5]
+
+
+@pytest.mark.parametrize("g", [1, 2, 3, 4, 9])
+def test_variant_zero_query_moments(g):
+    geom = small_geom(fh=5, fw=7, C=2, F=8, g=g)
+    inp = small_inputs(geom)
+    inp.q[:] = 0.0
+    S = geom.tokens_per_frame
+    mv = moment_values(geom, inp.n_hist_frames)
+    inp.v_hist[:] = mv[: inp.n_hist_frames * S]
+    inp.v_cur[:] = mv[inp.n_hist_frames * S:]
+    n_hist, C = inp.n_hist_frames, geom.chunk_frames
+
+    def block(frames, rr, cc):
+        nf, nr, nc = len(frames), len(rr), len(cc)
+        return np.array([nf * nr * nc, sum(frames) * nr * nc, nf * nc * sum(rr), nf * nr * sum(cc),
+                         nf * nc * sum(x * x for x in rr), nf * nr * sum(x * x for x in cc)], float)
+
+    out_d = orc.path_attention(inp, 1, D_, variant=V_DPREV)
+    out_p = orc.path_attention(inp, 2, P_, variant=V_CELLS)
+    frames_d = list(range(n_hist - C, n_hist + C))
+    for t in range(geom.lq):
+        want = block(frames_d, range(geom.frame_h), range(geom.frame_w))
+        assert np.allclose(out_d[t, :6], want / want[0], atol=1e-12, rtol=0)
+        qr, qc = (t % S) // geom.frame_w, t % geom.frame_w
+        rr = [r for r in range(geom.frame_h) if r // g == qr // g]          # the cell, by scanning rows
+        cc = [c for c in range(geom.frame_w) if c // g == qc // g]
+        want = block(list(range(n_hist + C)), rr, cc)
+        assert np.allclose(out_p[t, :6], want / want[0], atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("F,C", [(21, 3), (5, 1), (6, 3), (12, 2)])
+def test_variant_dummy_buffer_holds_latest_block(F, C):
+    for n in range(0, 12):
+        tab = orc.slot_table([S_, D_, P_, G_], F, C, n, variant=V_DPREV)
+        want = -np.ones(F - C, np.int32)
+        if n > 0:
+            # the latest finished block while rolling blocks exist, else the sink block
+            b = n - 1 if F // C > 2 else 0
+            want[:C] = np.arange(b * C, b * C + C)
+        assert np.array_equal(tab[1], want)
+        assert np.array_equal(tab[[0, 2, 3]], orc.slot_table([S_, P_, G_], F, C, n))
