@@ -188,6 +188,35 @@ def ablation(res, steps, warmup):
     return out
 
 
+def deployed_variants(name, steps, warmup):
+    """The pages' deployed paths (Spatial heads on 10 x 10 cells over every window
+    frame, Dummy heads with the previous block) on the same layer, against its full
+    window."""
+    import dataclasses
+    import torch
+    from head_routed_sparse_amd import headcast as hc
+    from head_routed_sparse_amd import inputs as hin
+    inp = hin.config_inputs(name)
+    g = dataclasses.replace(inp.geom, grid_h=10, grid_w=10)
+    dev = lambda a: torch.from_numpy(a).to(torch.bfloat16).cuda()  # noqa: E731
+    q, kh, vh, kc, vc = (dev(a) for a in (inp.q, inp.k_hist, inp.v_hist, inp.k_cur, inp.v_cur))
+    res = {}
+    for tag, labels, var in (("deployed", inp.labels, 3), ("full_window", np.full(g.num_heads, 3, np.int32), 0)):
+        buf = hc.hc_build_head_buffers(hc.make_desc(g, var), labels, kh, vh, inp.n_hist_frames)
+        ws = hc.routed_workspace(buf)
+        o = torch.empty_like(q)
+        hc.hc_timing_read()
+        hc.hc_timing_enable(True)
+        res[tag + "_ms"] = round(time_calls(lambda: hc.hc_routed_attention(buf, q, kc, vc, out=o, workspace=ws),
+                                            steps, warmup), 4)
+        hc.hc_timing_enable(False)
+        res[tag + "_kernel_avg_ms"] = {k: round(v[0] / v[1], 4) for k, v in hc.hc_timing_read().items() if v[1]}
+        del buf, ws, o
+    res["speedup_vs_full_window"] = round(res["full_window_ms"] / res["deployed_ms"], 3)
+    res["workload"] = f"{name}: Spatial heads on 10x10 cells in all window frames, Dummy heads + previous block"
+    return res
+
+
 def full_step(steps, warmup):
     """The 30-layer 720P step with planted heads: classify every layer once (labels
     must equal the planted ones), build its buffers, then time one denoise step =
@@ -334,6 +363,8 @@ def main():
                                          (sec["routed"]["kernels"]["dense"][0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "classify_ms": round(sec["classify_ms"], 3)}
         del sec
+    print("[bench] deployed path variants", file=sys.stderr, flush=True)
+    out["deployed_variants"] = {n: deployed_variants(n, max(3, a.steps // 4), 2) for n in ("720p", "1080p")}
     print("[bench] table-4 style ablation", file=sys.stderr, flush=True)
     out["ablation_720p"] = ablation(main_res, max(3, a.steps // 2), 2)
     if a.full_step:
