@@ -21,7 +21,6 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
   using L = AttnLds<D>;
   constexpr int KS = D / 16;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * L::bufElems];
-  __shared__ __attribute__((aligned(16))) int kcoord[2][kKeyTile];
 
   const SpatialEntry e = p.e[blockIdx.y];
   const int tr = blockIdx.x / p.tiles_c, tc = blockIdx.x % p.tiles_c;
@@ -63,27 +62,65 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
   const int nh = p.n_hist_frames;
 
   TileRegs<D> regs;
-  // element offset of local key j of tile t: frame t / nchunk of the history, or of the
-  // current block (cell mode, frames nh..), at the union position of chunk t % nchunk
-  auto key_off = [&](int t, int j, bool& cur) -> int64_t {
-    const int f = t / nchunk;
-    const int ui = min((t - f * nchunk) * kKeyTile + j, nU - 1);
-    const int kr = ur0 + ui / UW, kcol = uc0 + ui % UW;
-    cur = f >= nh;
-    const int64_t tok = (int64_t)(cur ? f - nh : f) * S + (int64_t)kr * fw + kcol;
-    return tok * (cur ? ts : hs);
+  constexpr int cpr = TileRegs<D>::cpr;
+  // Tiles are walked chunk-outer, frame-inner: tile t = chunk t / n_frames of the window
+  // union, in frame t % n_frames. The union position of every key a thread stages, and
+  // every lane's mask bits, depend only on the chunk, so they are computed once per chunk.
+  int tok_k[TileRegs<D>::kChunks], tok_v[4];   // within-frame token offsets of the staged rows
+  int cached_u = -1;
+  auto union_tok = [&](int u, int j) {
+    const int ui = min(u * kKeyTile + j, nU - 1);
+    const int q = ui / UW;
+    return (ur0 + q) * fw + uc0 + (ui - q * UW);
   };
   auto load = [&](int t) {
-    load_tile<D>(regs, [&](int j) { bool c; const int64_t o = key_off(t, j, c); return (c ? kcb : kh) + o; },
-                 [&](int j) { bool c; const int64_t o = key_off(t, j, c); return (c ? vcb : vh) + o; }, tid);
-  };
-  auto store = [&](int t, int b) {
-    if (tid < kKeyTile) {
-      const int f = t / nchunk;
-      const int ui = (t - f * nchunk) * kKeyTile + tid;
-      kcoord[b][tid] = ui < nU ? (((ur0 + ui / UW) << 16) | (uc0 + ui % UW)) : 0x7FFF0000;
+    const int u = t / n_frames, f = t - u * n_frames;
+    if (u != cached_u) {
+      cached_u = u;
+#pragma unroll
+      for (int i = 0; i < TileRegs<D>::kChunks; ++i) tok_k[i] = union_tok(u, (tid + 256 * i) / cpr);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) tok_v[jj] = union_tok(u, 4 * (tid % 16) + jj);
     }
-    store_tile<D>(regs, lds + b * L::bufElems, tid);
+    const bool cur = f >= nh;
+    const int64_t stride = cur ? ts : hs;
+    const int64_t fbase = (int64_t)(cur ? f - nh : f) * S * stride;
+    const uint16_t* kb = (cur ? kcb : kh) + fbase;
+    const uint16_t* vb = (cur ? vcb : vh) + fbase;
+#pragma unroll
+    for (int i = 0; i < TileRegs<D>::kChunks; ++i)
+      regs.k[i] = *(const u32x4*)(kb + (int64_t)tok_k[i] * stride + ((tid + 256 * i) % cpr) * 8);
+#pragma unroll
+    for (int i = 0; i < TileRegs<D>::vPer; ++i) {
+      const int uu = tid + 256 * i;
+      if (uu < TileRegs<D>::vUnits) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          regs.v[i][jj] = *(const u32x4*)(vb + (int64_t)tok_v[jj] * stride + (uu / 16) * 8);
+      }
+    }
+  };
+  // Bit kb*16 + r: key score_key(kb, r, half) of chunk u lies in this lane's window.
+  auto mask_bits = [&](int u) {
+    uint32_t bits = 0;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int ui0 = u * kKeyTile + score_key(kb, 4 * a, half);
+        int ur = ui0 / UW, uc = ui0 - ur * UW;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const bool in = ui0 + b < nU && (unsigned)(ur0 + ur - r0q) < (unsigned)ehq &&
+                          (unsigned)(uc0 + uc - c0q) < (unsigned)ewq;
+          bits |= (uint32_t)in << (kb * 16 + 4 * a + b);
+          if (++uc == UW) {
+            uc = 0;
+            ++ur;
+          }
+        }
+      }
+    return bits;
   };
 
   for (int cf0 = 0; cf0 < p.chunk_frames; cf0 += nwave) {
@@ -97,34 +134,20 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
 
     AttnState<D> st;
     st.init();
+    cached_u = -1;
     if (n_tiles > 0) {
       load(0);
-      store(0, 0);
+      store_tile<D>(regs, lds, tid);
     }
     __syncthreads();
+    uint32_t bits = 0;
     for (int t = 0; t < n_tiles; ++t) {
       const bool more = t + 1 < n_tiles;
       if (more) load(t + 1);
-      const uint16_t* buf = lds + (t & 1) * L::bufElems;
-      const int* kcd = kcoord[t & 1];
-      int kr4[2][4][4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int4 v = *(const int4*)(kcd + kb * 32 + 8 * a + 4 * half);
-          kr4[kb][a][0] = v.x;
-          kr4[kb][a][1] = v.y;
-          kr4[kb][a][2] = v.z;
-          kr4[kb][a][3] = v.w;
-        }
-      attend_tile<D, true>(st, qreg, buf, p.scale_log2, l32, half, [&](int kb, int r) {
-        const int kc2 = kr4[kb][r >> 2][r & 3];
-        const unsigned dr = (unsigned)((kc2 >> 16) - r0q);
-        const unsigned dc = (unsigned)((kc2 & 0xFFFF) - c0q);
-        return dr < (unsigned)ehq && dc < (unsigned)ewq;
-      });
-      if (more) store(t + 1, (t + 1) & 1);
+      if (t % n_frames == 0) bits = mask_bits(t / n_frames);
+      attend_tile<D, true>(st, qreg, lds + (t & 1) * L::bufElems, p.scale_log2, l32, half,
+                           [&](int kb, int r) { return ((bits >> (kb * 16 + r)) & 1u) != 0; });
+      if (more) store_tile<D>(regs, lds + ((t + 1) & 1) * L::bufElems, tid);
       __syncthreads();
     }
 
