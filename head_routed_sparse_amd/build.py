@@ -12,6 +12,9 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libheadcast.so")
 SOURCES = ["hc_api.cpp", "hc_dense.hip", "hc_spatial.hip", "hc_aux.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# The dense kernel keeps its MFMA accumulators in VGPRs: its softmax reads the scores
+# and its rare O rescale multiplies the accumulators without AGPR round trips.
+PER_FILE = {}
 # Packed fp32 VALU forms are switched off for all device code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -20,6 +23,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     extra = ["-fno-honor-nans"] if src.endswith(".hip") else []   # kernels: no NaN canonicalisation
+    extra += PER_FILE.get(src, [])
     cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
