@@ -155,7 +155,7 @@ struct Entry {
   int32_t hist_len, cur_len, head, nsplit, split_len, slot;
 };
 
-constexpr int kSlotsPerCu = 1;    // dense workgroups resident per CU (one wave per SIMD)
+constexpr int kSlotsPerCu = 2;    // dense workgroups resident per CU
 constexpr int kNumCu = 256;
 constexpr double kItemOverheadTiles = 3.0;
 

@@ -2,16 +2,17 @@
 // current-block part of the Spatial path, and the classifier's reference and block
 // proxies (HeadCast Sec. 4.4 "Head-Specific Attention"; Sec. 4.2 Eq. 2).
 //
-// One workgroup = 256 queries of one head against one key range: a split of the
+// One workgroup = 128 queries of one head against one key range: a split of the
 // head's [history rows ; current-block rows]. History rows come from the compact
 // per-head buffer (stride D) or, for the classifier, from the monolithic cache
 // (stride H*D); current-block rows are read in place from [C*S][H][D]. Items are
 // ordered longest first and grouped per XCD so that the query tiles sharing a key
 // range run on the same L2.
 //
-// For D=128 the workgroup has eight waves of 32 queries (two waves per SIMD, all
-// state in VGPRs); for D=64, four waves of two 32-query blocks, where each K or V
-// fragment read from LDS feeds one MFMA per block. Keys advance in steps of 32. The
+// For D=128 the workgroup has four waves of 32 queries (one per SIMD, all state in
+// VGPRs) and two workgroups share a CU, each with its own LDS ring and barrier, so
+// that one's softmax overlaps the other's MFMAs; for D=64, two waves of two 32-query
+// blocks, where each K or V fragment read from LDS feeds one MFMA per block. Keys advance in steps of 32. The
 // K and V rows of a step travel from global memory straight into a ring of LDS
 // stages (16-byte direct loads, no staging registers), row-major, with the 16-byte
 // chunks of row r permuted (chunk c stored at c ^ swz(r)) so that the K fragment
@@ -33,7 +34,7 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 template <int D, int QB>
 struct Ring {
-  static constexpr int kWaves = 8 / QB;                    // waves per workgroup
+  static constexpr int kWaves = kDenseQ / (32 * QB);       // waves per workgroup
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kCpr = D / 8;                       // 16-byte chunks per row
   static constexpr int kTileBytes = kStep * kRowBytes;     // the K (or V) rows of a step
@@ -87,9 +88,18 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
 template <int D>
 struct Block {
   f32x16 o[D / 32];
-  float m;   // running max, log2 units with the scale folded in
+  float m;   // reference max, log2 units with the scale folded in
   float l;   // this lane's share of the running sum
 };
+
+// Until the first step has set it, m holds this finite stand-in for minus infinity:
+// every finite score then exponentiates to +inf and forces the first rescale, while
+// masked scores (-inf) still give exactly 0 (no inf - inf).
+constexpr float kNoMax = -1e30f;
+// The reference max only moves when a step's probabilities would exceed this sum per
+// lane (2^64): p stays far inside the fp32 and bf16 ranges, and precision does not
+// depend on the scale, so no per-step row maximum is needed.
+constexpr float kSumLimit = 18446744073709551616.0f;
 
 // Row max of a step's scores across both lane halves.
 __device__ __forceinline__ float step_max(const f32x16& s) {
@@ -100,44 +110,57 @@ __device__ __forceinline__ float step_max(const f32x16& s) {
   return max_halves(m);
 }
 
-// Lazy rescale: the running max only moves when the step's max exceeds it by more
-// than kRescaleSlack (log2 units), so p stays below 2^kRescaleSlack.
-template <int D>
-__device__ __forceinline__ void maybe_rescale(Block<D>& b, float mx, float c) {
-  const float mt = mx * c;
-  if (__builtin_amdgcn_ballot_w64(mt > b.m + kRescaleSlack)) {
-    const float m_new = __builtin_fmaxf(b.m, mt);
-    const float f = (m_new == -INFINITY) ? 1.f : fast_exp2(b.m - m_new);
-    b.l *= f;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {   // one accumulator block at a time
-#pragma unroll
-      for (int r = 0; r < 16; ++r) b.o[db][r] *= f;
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    b.m = m_new;
-  }
-}
-
 // p = exp2(s c - m) packed to bf16 pairs (register r of the scores = element r of the
-// B operand of the PV product); the running sum adds the same rounded p.
-template <int D>
-__device__ __forceinline__ void exponentiate(Block<D>& b, const f32x16& s, float c, u32x4 (&pk)[2]) {
-  const float m_sub = (b.m == -INFINITY) ? 0.f : b.m;
+// B operand of the PV product); returns this lane's sum of the same rounded p.
+__device__ __forceinline__ float exponentiate(const f32x16& s, float m, float c, u32x4 (&pk)[2]) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  float ls = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float p0 = fast_exp2(__builtin_fmaf(s[2 * e], c, -m_sub));
-    const float p1 = fast_exp2(__builtin_fmaf(s[2 * e + 1], c, -m_sub));
+    const float p0 = fast_exp2(__builtin_fmaf(s[2 * e], c, -m));
+    const float p1 = fast_exp2(__builtin_fmaf(s[2 * e + 1], c, -m));
     const uint32_t w = pack_bf16(p0, p1);
     pk[e >> 2][e & 3] = w;
-    b.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, b.l, false);
+    ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, ls, false);
   }
+  return ls;
+}
+
+// Softmax of one step for every block: exponentiate against the reference max; in
+// the rare step where some lane's sum passes kSumLimit (always the first step), move
+// the reference max to the step's row max, rescale O and l, and exponentiate again.
+template <int D, int QB>
+__device__ __forceinline__ void softmax_step(Block<D> (&blk)[QB], const f32x16 (&sc)[QB], float c,
+                                             u32x4 (&pk)[QB][2]) {
+  float ls[QB];
+  bool over = false;
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    ls[b] = exponentiate(sc[b], blk[b].m, c, pk[b]);
+    over |= ls[b] > kSumLimit;
+  }
+  if (__builtin_amdgcn_ballot_w64(over)) {
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const float m_new = __builtin_fmaxf(blk[b].m, step_max(sc[b]) * c);
+      const float f = fast_exp2(blk[b].m - m_new);
+      blk[b].l *= f;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) blk[b].o[db][r] *= f;
+      blk[b].m = m_new;
+      ls[b] = exponentiate(sc[b], m_new, c, pk[b]);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < QB; ++b) blk[b].l += ls[b];
 }
 
 template <int D, int QB>
-__global__ __launch_bounds__(64 * (8 / QB), 1) void dense_attn_bf16(const DenseParams p) {
+__global__ __launch_bounds__(64 * (kDenseQ / (32 * QB)), kDenseQ / (32 * QB) >= 8 ? 1 : 8 / (kDenseQ / (32 * QB)))
+void dense_attn_bf16(const DenseParams p) {
   using R = Ring<D, QB>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -286,7 +309,7 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void dense_attn_bf16(const DenseP
   for (int b = 0; b < QB; ++b) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) blk[b].o[db] = f32x16{};
-    blk[b].m = -INFINITY;
+    blk[b].m = kNoMax;
     blk[b].l = 0.f;
   }
   const float c = p.scale_log2;
@@ -308,17 +331,11 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void dense_attn_bf16(const DenseP
     wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
   f32x16 s0[QB], s1[QB];   // scores of two consecutive steps
-  float mx[QB];
   scores(s0, (0 - r0) & 3);
-#pragma unroll
-  for (int b = 0; b < QB; ++b) mx[b] = step_max(s0[b]);
 
-  // step j on stage `stage` (scores in sc): rescale if needed, loads of step
-  // j+kStages-1, scores of step j+1 (into sn) beside the exponentials of step j, then
-  // PV of step j beside the row maxima of step j+1
+  // step j on stage `stage` (scores in sc): loads of step j+kStages-1, scores of
+  // step j+1 (into sn) beside the softmax of step j, then PV of step j
   auto step = [&](f32x16 (&sc)[QB], f32x16 (&sn)[QB], int stage, int j) {
-#pragma unroll
-    for (int b = 0; b < QB; ++b) maybe_rescale(blk[b], mx[b], c);
     if (j + kStages - 2 < n)
       wait_vmcnt<2 * R::kLoads * (kStages - 3)>();
     else
@@ -327,16 +344,11 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void dense_attn_bf16(const DenseP
     if (j + kStages - 1 < n) issue(j + kStages - 1, (stage + kStages - 1) & 3);
     scores(sn, (stage + 1) & 3);
     u32x4 pk[QB][2];
-#pragma unroll
-    for (int b = 0; b < QB; ++b) exponentiate(blk[b], sc[b], c, pk[b]);
-    pv(pk, stage);
-#pragma unroll
-    for (int b = 0; b < QB; ++b) mx[b] = step_max(sn[b]);
-    // issue in order: alternate each MFMA with the VALU work that fits under it, and
-    // read fragments kAhead MFMA groups ahead of their use
+    softmax_step(blk, sc, c, pk);
+    // issue in order: alternate each score MFMA with the exponentials that fit under
+    // it, and read K fragments kAhead MFMA groups ahead of their use
     constexpr int kAhead = 3;
-    constexpr int kVq = 6;   // VALU slots per MFMA while exponentiating
-    constexpr int kVm = 3;   // VALU slots per MFMA while reducing maxima
+    constexpr int kVq = 6;
     __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
@@ -346,17 +358,8 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void dense_attn_bf16(const DenseP
         __builtin_amdgcn_sched_group_barrier(0x002, kVq, 0);
       }
       if (i + kAhead < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (i + kAhead == KS) __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
     }
-#pragma unroll
-    for (int i = 0; i < 2 * DB; ++i) {
-#pragma unroll
-      for (int b = 0; b < QB; ++b) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, kVm, 0);
-      }
-      if (i + kAhead < 2 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
+    pv(pk, stage);
   };
 
   int j = 0;
@@ -377,19 +380,13 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void dense_attn_bf16(const DenseP
     const int valid = k_end - (k_begin + j * kStep);
     if (valid < kStep) {
 #pragma unroll
-      for (int b = 0; b < QB; ++b) {
+      for (int b = 0; b < QB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (8 * (r >> 2) + 4 * half + (r & 3) >= valid) s0[b][r] = -INFINITY;
-        mx[b] = step_max(s0[b]);
-      }
     }
     u32x4 pk[QB][2];
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      maybe_rescale(blk[b], mx[b], c);
-      exponentiate(blk[b], s0[b], c, pk[b]);
-    }
+    softmax_step(blk, s0, c, pk);
     pv(pk, 0);
   }
 
@@ -424,8 +421,7 @@ hipError_t launch_dense_f32(const DenseParams& p, int head_dim, hipStream_t s);
 hipError_t launch_dense(const DenseParams& p, int head_dim, int bf16, hipStream_t s) {
   if (p.n_items == 0) return hipSuccess;
   if (!bf16) return launch_dense_f32(p, head_dim, s);
-  // D=128: eight waves of 32 queries (two per SIMD); D=64: four waves of 64 queries,
-  // since a 64-wide step tile is too small for eight loading waves
+  // D=128: four waves of 32 queries; D=64: two waves of 64 queries
   const dim3 grid(dense_items_grid(p.n_items, p.xcd_group));
   if (head_dim == 64)
     hipLaunchKernelGGL((dense_attn_bf16<64, 2>), grid, dim3(64 * Ring<64, 2>::kWaves), 0, s, p);

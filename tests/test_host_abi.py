@@ -123,7 +123,7 @@ def test_routed_plan_covers_every_key_once(name, next_block):
     for lab in (labels, np.full(g.num_heads, 3, np.int32)):
         pb = hc.hc_plan_head_buffers(hc.make_desc(g), lab, next_block)
         ents, n_items = hc.hc_debug_routed_plan(pb)
-        nqt = -(-g.lq // 256)
+        nqt = -(-g.lq // 128)
         hist_blocks = orc.window_history_blocks(next_block, g.window_frames, g.chunk_frames)
         assert sorted(ents[:, 0]) == list(range(g.num_heads))
         begin = 0
