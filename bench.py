@@ -338,7 +338,7 @@ def main():
         "full_window_kernel_avg_ms": {k: round(v[0], 4) for k, v in base["kernels"].items()},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(a.config),
-                     "kernel": "dense_attn_bf16<128>", "flops_per_launch": dflops},
+                     "kernel": "dense_attn_bf16<128, 1>", "flops_per_launch": dflops},
         "full_window_roofline_frac": round(dense_flops(g, base["labels"], n_hist) /
                                            (base["kernels"]["dense"][0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "spatial_gather": {"flops": sp_flops, "unique_bytes": sp_bytes,

@@ -90,6 +90,34 @@ def test_one_block_window_all_paths_agree():
         assert_close(got[:, h], orc.path_attention(inp, h, G_), *TOL["bf16"])
 
 
+@pytest.mark.parametrize("jumps", [(0, 20, 45, 110), (110, 0, 70, 30), (5, 5, 5, 200)])
+def test_rescale_when_scores_jump(jumps):
+    """Scores that rise by tens to hundreds of log2 units part-way through the key
+    range (a shared direction added to every query and, with growing weight, to the
+    keys of later frames): the GPU's reference max must move mid-stream, rescaling O
+    and the running sum, and agree with the oracle's exact softmax."""
+    g = hin.Geometry(4, 128, 6, 11, 2, 10, 3, 3, "bf16")
+    inp = hin.generate(g, (G_, S_, P_, G_), seed=11)
+    S, C, d = g.tokens_per_frame, g.chunk_frames, g.head_dim
+    rng = np.random.default_rng(12)
+    u = rng.standard_normal(d).astype(np.float32)
+    u /= np.linalg.norm(u)
+    c = g.softmax_scale * np.log2(np.e)
+    inp.q[:] = hin.round_to_bf16(inp.q + u)
+    n_hist = inp.n_hist_frames
+    # frame groups: history frames split in three, then the current block
+    groups = np.array_split(np.arange(n_hist), 3)
+    for gi, frames in enumerate(groups):
+        for f in frames:
+            inp.k_hist[f * S:(f + 1) * S] += (jumps[gi] / c) * u
+    inp.k_cur += (jumps[3] / c) * u
+    inp.k_hist[:] = hin.round_to_bf16(inp.k_hist)
+    inp.k_cur[:] = hin.round_to_bf16(inp.k_cur)
+    got, _, _ = run_routed(inp)
+    want = orc.routed_attention(inp)
+    print(jumps, assert_close(got, want, *TOL["bf16"], what=f"jumps {jumps}"))
+
+
 def test_zero_query_key_set_moments():
     """q = 0 gives the mean of V over the key set: V columns (1, frame, row, col, row^2,
     col^2) pin every path's membership on the GPU (values exact in bf16)."""
