@@ -67,7 +67,7 @@ def spatial_work(geom, labels, n_hist):
     return flops, byts
 
 
-KERNEL_SOURCES = ["hc_dense.hip", "hc_tile.h", "hc_mfma.h", "hc_internal.h"]
+KERNEL_SOURCES = ["hc_dense.hip", "hc_pipe.h", "hc_mfma.h", "hc_internal.h"]
 COUNTERS = os.path.join(ROOT, "profiles", "dense_attn_bf16_720p_counters.json")
 
 

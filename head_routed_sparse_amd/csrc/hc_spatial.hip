@@ -4,13 +4,16 @@
 // window whose origin is clamp(r - g/2, 0, fh - g) x clamp(c - g/2, 0, fw - g).
 //
 // A workgroup (4 waves) takes a tile of 4 x 8 positions of one Spatial head, one wave
-// per chunk frame (the chunk frames at one position share the key set exactly). For each
-// history frame it walks the union of the 32 windows in 64-key LDS tiles: K/V rows
-// are gathered as whole 256-B rows (coalesced), scores come from the same MFMA tile
-// step as the dense path, and keys outside a query's own window are masked.
-// In final mode the result is merged with the dense current-block partial by its
-// log-sum-exp and written as bf16; in partial mode (classifier) it is stored as fp32.
-#include "hc_tile.h"
+// per chunk frame (the chunk frames at one position share the key set exactly; with
+// three chunk frames the fourth wave only loads). It walks the union of the 32
+// windows in 32-key steps, chunk-outer and frame-inner, on the dense kernel's pipeline
+// (hc_pipe.h): every step's rows are gathered whole (256 B) by 16-byte direct loads
+// into the LDS ring, and keys outside a query's own window are masked. The union
+// position of every row a lane loads, and every lane's mask bits, depend only on the
+// chunk, so they are computed once per chunk. In final mode the result is merged with
+// the dense current-block partial by its log-sum-exp and written as bf16; in partial
+// mode (classifier) it is stored as fp32; with cells the whole key set is walked here.
+#include "hc_pipe.h"
 
 namespace hc {
 
@@ -18,9 +21,12 @@ namespace {
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams p) {
-  using L = AttnLds<D>;
+  constexpr int W = 4;
+  using R = Ring<D, 1, W>;
   constexpr int KS = D / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * L::bufElems];
+  constexpr int DB = D / 32;
+  __shared__ __attribute__((aligned(1024))) char ring[R::kBytes];
+  lds_char* const lds = (lds_char*)ring;
 
   const SpatialEntry e = p.e[blockIdx.y];
   const int tr = blockIdx.x / p.tiles_c, tc = blockIdx.x % p.tiles_c;
@@ -38,14 +44,14 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
   const int uc0 = org_c(C0), uc1 = org_c(C1) + ext_c(C1);
   const int UW = uc1 - uc0;
   const int nU = (ur1 - ur0) * UW;
-  const int nchunk = (nU + kKeyTile - 1) / kKeyTile;
+  const int nchunk = (nU + kStep - 1) / kStep;
   // frames walked: the history (and, for cells, the current block after it)
-  const int n_frames = p.n_hist_frames + (cells ? p.chunk_frames : 0);
-  const int n_tiles = n_frames * nchunk;
+  const int nh = p.n_hist_frames;
+  const int n_frames = nh + (cells ? p.chunk_frames : 0);
+  const int n = nchunk * n_frames;   // steps
 
   const int tid = threadIdx.x;
-  constexpr int nwave = 4;   // one wave per chunk frame; spare waves only load
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int half = lane >> 5;
@@ -54,132 +60,123 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
   const int r0q = org_r(min(pr, fh - 1)), ehq = ext_r(min(pr, fh - 1));
   const int c0q = org_c(min(pc, fw - 1)), ewq = ext_c(min(pc, fw - 1));
 
-  const uint16_t* kh = (const uint16_t*)p.k_hist + e.hist_off;
-  const uint16_t* vh = (const uint16_t*)p.v_hist + e.hist_off;
-  const uint16_t* kcb = cells ? (const uint16_t*)p.k_cur + (int64_t)e.head * D : kh;
-  const uint16_t* vcb = cells ? (const uint16_t*)p.v_cur + (int64_t)e.head * D : vh;
-  const int64_t hs = p.hist_stride, ts = p.tok_stride;
-  const int nh = p.n_hist_frames;
+  const char* kh = (const char*)p.k_hist + e.hist_off * 2;
+  const char* vh = (const char*)p.v_hist + e.hist_off * 2;
+  const char* kcb = cells ? (const char*)p.k_cur + (int64_t)e.head * D * 2 : kh;
+  const char* vcb = cells ? (const char*)p.v_cur + (int64_t)e.head * D * 2 : vh;
+  const int64_t hs = p.hist_stride * 2, ts = p.tok_stride * 2;   // bytes
 
-  TileRegs<D> regs;
-  constexpr int cpr = TileRegs<D>::cpr;
-  // Tiles are walked chunk-outer, frame-inner: tile t = chunk t / n_frames of the window
-  // union, in frame t % n_frames. The union position of every key a thread stages, and
-  // every lane's mask bits, depend only on the chunk, so they are computed once per chunk.
-  int tok_k[TileRegs<D>::kChunks], tok_v[4];   // within-frame token offsets of the staged rows
-  int cached_u = -1;
-  auto union_tok = [&](int u, int j) {
-    const int ui = min(u * kKeyTile + j, nU - 1);
-    const int q = ui / UW;
-    return (ur0 + q) * fw + uc0 + (ui - q * UW);
+  LaneAddr<D, 1, W> la;
+  la.init(wave, lane);
+  // token (row * fw + col within a frame) of union index i
+  auto union_tok = [&](int i) {
+    i = min(i, nU - 1);
+    const int q = i / UW;
+    return (ur0 + q) * fw + uc0 + (i - q * UW);
   };
-  auto load = [&](int t) {
-    const int u = t / n_frames, f = t - u * n_frames;
-    if (u != cached_u) {
-      cached_u = u;
+
+  for (int cf0 = 0; cf0 < p.chunk_frames; cf0 += W) {
+    const int cf = cf0 + wave;
+    const bool active = cf < p.chunk_frames;   // wave-uniform
+    const bool q_ok = pos_ok && active;
+    const int q_row = min(cf, p.chunk_frames - 1) * S + min(pr, fh - 1) * fw + min(pc, fw - 1);
+    const uint16_t* qp = (const uint16_t*)p.q + (int64_t)q_row * p.tok_stride + (int64_t)e.head * D;
+    u32x4 q[1][KS];
 #pragma unroll
-      for (int i = 0; i < TileRegs<D>::kChunks; ++i) tok_k[i] = union_tok(u, (tid + 256 * i) / cpr);
+    for (int ks = 0; ks < KS; ++ks) q[0][ks] = *(const u32x4*)(qp + ks * 16 + half * 8);
+
+    // loads: step t = chunk t / n_frames of the union in frame t % n_frames, issued in order
+    int iu = 0, ifr = 0;
+    int tok[R::kLoads];
+    auto issue = [&](int, int stage) {
+      if (ifr == 0) {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) tok_v[jj] = union_tok(u, 4 * (tid % 16) + jj);
-    }
-    const bool cur = f >= nh;
-    const int64_t stride = cur ? ts : hs;
-    const int64_t fbase = (int64_t)(cur ? f - nh : f) * S * stride;
-    const uint16_t* kb = (cur ? kcb : kh) + fbase;
-    const uint16_t* vb = (cur ? vcb : vh) + fbase;
-#pragma unroll
-    for (int i = 0; i < TileRegs<D>::kChunks; ++i)
-      regs.k[i] = *(const u32x4*)(kb + (int64_t)tok_k[i] * stride + ((tid + 256 * i) % cpr) * 8);
-#pragma unroll
-    for (int i = 0; i < TileRegs<D>::vPer; ++i) {
-      const int uu = tid + 256 * i;
-      if (uu < TileRegs<D>::vUnits) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          regs.v[i][jj] = *(const u32x4*)(vb + (int64_t)tok_v[jj] * stride + (uu / 16) * 8);
+        for (int i = 0; i < R::kLoads; ++i) tok[i] = union_tok(iu * kStep + la.ld_row[i]);
       }
-    }
-  };
-  // Bit kb*16 + r: key score_key(kb, r, half) of chunk u lies in this lane's window.
-  auto mask_bits = [&](int u) {
+      const bool cur = ifr >= nh;
+      const int64_t stride = cur ? ts : hs;
+      const int64_t fbase = (int64_t)(cur ? ifr - nh : ifr) * S * stride;
+      const char* kb = (cur ? kcb : kh) + fbase;
+      const char* vb = (cur ? vcb : vh) + fbase;
+#pragma unroll
+      for (int i = 0; i < R::kLoads; ++i) {
+        const uint32_t off = (uint32_t)(tok[i] * stride) + la.ld_chunk[i];
+        dma16(kb, off, la.dst(lds, stage, wave, i, 0));
+        dma16(vb, off, la.dst(lds, stage, wave, i, 1));
+      }
+      if (++ifr == n_frames) {
+        ifr = 0;
+        ++iu;
+      }
+    };
+    // masks, in step order: bit r = key step_key(r, half) of the chunk lies in this
+    // lane's window (and in the union)
+    int mu = 0, mf = 0;
     uint32_t bits = 0;
+    auto mask = [&](f32x16 (&sc)[1]) {
+      if (mf == 0) {
+        bits = 0;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int a = 0; a < 4; ++a) {
+          const int i0 = mu * kStep + 8 * a + 4 * half;
+          int ur = i0 / UW, uc = i0 - ur * UW;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int ui0 = u * kKeyTile + score_key(kb, 4 * a, half);
-        int ur = ui0 / UW, uc = ui0 - ur * UW;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const bool in = ui0 + b < nU && (unsigned)(ur0 + ur - r0q) < (unsigned)ehq &&
-                          (unsigned)(uc0 + uc - c0q) < (unsigned)ewq;
-          bits |= (uint32_t)in << (kb * 16 + 4 * a + b);
-          if (++uc == UW) {
-            uc = 0;
-            ++ur;
+          for (int b = 0; b < 4; ++b) {
+            const bool in = i0 + b < nU && (unsigned)(ur0 + ur - r0q) < (unsigned)ehq &&
+                            (unsigned)(uc0 + uc - c0q) < (unsigned)ewq;
+            bits |= (uint32_t)in << (4 * a + b);
+            if (++uc == UW) {
+              uc = 0;
+              ++ur;
+            }
           }
         }
       }
-    return bits;
-  };
-
-  for (int cf0 = 0; cf0 < p.chunk_frames; cf0 += nwave) {
-    const int cf = cf0 + wave;
-    const bool q_ok = pos_ok && cf < p.chunk_frames;
-    const int q_row = min(cf, p.chunk_frames - 1) * S + min(pr, fh - 1) * fw + min(pc, fw - 1);
-    const uint16_t* qp = (const uint16_t*)p.q + (int64_t)q_row * p.tok_stride + (int64_t)e.head * D;
-    u32x4 qreg[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qreg[ks] = *(const u32x4*)(qp + ks * 16 + half * 8);
+      for (int r = 0; r < 16; ++r)
+        if (!((bits >> r) & 1u)) sc[0][r] = -INFINITY;
+      if (++mf == n_frames) {
+        mf = 0;
+        ++mu;
+      }
+    };
 
-    AttnState<D> st;
-    st.init();
-    cached_u = -1;
-    if (n_tiles > 0) {
-      load(0);
-      store_tile<D>(regs, lds, tid);
-    }
-    __syncthreads();
-    uint32_t bits = 0;
-    for (int t = 0; t < n_tiles; ++t) {
-      const bool more = t + 1 < n_tiles;
-      if (more) load(t + 1);
-      if (t % n_frames == 0) bits = mask_bits(t / n_frames);
-      attend_tile<D, true>(st, qreg, lds + (t & 1) * L::bufElems, p.scale_log2, l32, half,
-                           [&](int kb, int r) { return ((bits >> (kb * 16 + r)) & 1u) != 0; });
-      if (more) store_tile<D>(regs, lds + ((t + 1) & 1) * L::bufElems, tid);
-      __syncthreads();
-    }
+    Block<D> blk[1];
+    init_blocks(blk);
+    if (n > 0) run_steps<D, 1, W, true>(n, lds, la, q, blk, p.scale_log2, active, issue, mask);
+    __syncthreads();   // the ring is reused by the next group of chunk frames
 
-    const float l_tot = sum_halves(st.l_run);
+    const float l_tot = sum_halves(blk[0].l);
+    const float m_s = blk[0].m;
     if (q_ok) {
       if (cells) {   // the whole key set was walked here: normalise and write
         uint16_t* op = (uint16_t*)p.out + (int64_t)q_row * p.tok_stride + (int64_t)e.head * D;
-        store_out_bf16<D>(st, 1.0f / l_tot, op, half);
+        store_out_bf16<D>(blk[0], 1.0f / l_tot, op, half);
       } else if (e.out_slot >= 0) {
         const int64_t prow = (int64_t)e.out_slot * p.lq + q_row;
-        store_partial<D>(st, l_tot, p.part_o + prow * D, p.part_ml + prow * 2, half);
+        store_partial<D>(blk[0], l_tot, p.part_o + prow * D, p.part_ml + prow * 2, half);
       } else {
-        // merge with the dense current-block partial by log-sum-exp
+        // merge with the dense current-block partial by log-sum-exp (an empty history
+        // leaves m_s at the finite stand-in and weight 0)
         const int64_t crow = (int64_t)e.cur_slot * p.lq + q_row;
         const float m_c = p.part_ml[crow * 2], l_c = p.part_ml[crow * 2 + 1];
-        const float M = fmaxf(st.m_run, m_c);
-        const float wa = st.m_run == -INFINITY ? 0.f : fast_exp2(st.m_run - M);
+        const float M = fmaxf(m_s, m_c);
+        const float wa = fast_exp2(m_s - M);
         const float wc = fast_exp2(m_c - M);
         const float inv = 1.0f / (wa * l_tot + wc * l_c);
         const float* po = p.part_o + crow * D;
         uint16_t* op = (uint16_t*)p.out + (int64_t)q_row * p.tok_stride + (int64_t)e.head * D;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int a = 0; a < 4; ++a) {
             const int d = db * 32 + 8 * a + 4 * half;
             const f32x4 oc = *(const f32x4*)(po + d);
             u32x2 w;
-            w[0] = pack_bf16((wa * st.o[db][4 * a] + wc * oc[0]) * inv,
-                             (wa * st.o[db][4 * a + 1] + wc * oc[1]) * inv);
-            w[1] = pack_bf16((wa * st.o[db][4 * a + 2] + wc * oc[2]) * inv,
-                             (wa * st.o[db][4 * a + 3] + wc * oc[3]) * inv);
+            w[0] = pack_bf16((wa * blk[0].o[db][4 * a] + wc * oc[0]) * inv,
+                             (wa * blk[0].o[db][4 * a + 1] + wc * oc[1]) * inv);
+            w[1] = pack_bf16((wa * blk[0].o[db][4 * a + 2] + wc * oc[2]) * inv,
+                             (wa * blk[0].o[db][4 * a + 3] + wc * oc[3]) * inv);
             *(u32x2*)(op + d) = w;
           }
       }
