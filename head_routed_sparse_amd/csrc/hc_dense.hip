@@ -125,7 +125,7 @@ void dense_attn_bf16(const DenseParams p) {
 
   Block<D> blk[QB];
   init_blocks(blk);
-  run_steps<D, QB, W, false>(n, lds, la, q, blk, p.scale_log2, true, issue, mask_last);
+  run_steps<D, QB, W, false>(n, lds, la, q, blk, p.scale_log2, true, issue, [] {}, mask_last);
 
   // outputs
 #pragma unroll

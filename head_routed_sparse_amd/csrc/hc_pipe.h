@@ -231,18 +231,21 @@ struct LaneAddr {
 // The step pipeline over n >= 1 steps of 32 keys for W waves of QB query blocks.
 //   issue(t, stage): start the direct loads of step t into ring stage `stage` (called
 //                    once for t = 0, 1, 2, ... in order);
-//   mask(sc):        edit the scores of the next step before its softmax (called once
-//                    per step, in order, when kMaskEvery; else only for the last step).
+//   prep():          get ready to mask the next step (may branch; called once per step,
+//                    in order, before that step's score MFMAs are issued, when kMaskEvery);
+//   mask(sc):        edit the scores of the next step before its softmax, without
+//                    branching (called once per step, in order, when kMaskEvery; else
+//                    only for the last step).
 // Step t sits on ring stage (t - r0) mod 4 with r0 = (n - 1) mod 4: the first r0 steps
 // run with run-time stage offsets, the other n - 1 - r0 (a multiple of 4) in groups of
 // four with the offsets folded into the LDS instructions, and the last step lands on
 // stage 0.
 //   active:          false for a wave with no queries of its own: it still issues its
 //                    share of the loads and meets every barrier, but skips the math.
-template <int D, int QB, int W, bool kMaskEvery, class Issue, class Mask>
+template <int D, int QB, int W, bool kMaskEvery, class Issue, class Prep, class Mask>
 __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D, QB, W>& la,
                                           const u32x4 (&q)[QB][D / 16], Block<D> (&blk)[QB], float c,
-                                          bool active, Issue&& issue, Mask&& mask) {
+                                          bool active, Issue&& issue, Prep&& prep, Mask&& mask) {
   using R = Ring<D, QB, W>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -299,6 +302,7 @@ __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D
     __builtin_amdgcn_s_barrier();
     if (j + kStages - 1 < n) issue(j + kStages - 1, (stage + kStages - 1) & 3);
     if (!active) return;
+    if (kMaskEvery) prep();
     scores(sn, (stage + 1) & 3);
     if (kMaskEvery) mask(sc);
     u32x4 pk[QB][2];
@@ -334,6 +338,7 @@ __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D
   }
   // last step (stage 0, scores in s0)
   if (!active) return;
+  if (kMaskEvery) prep();
   mask(s0);
   u32x4 pk[QB][2];
   softmax_step(blk, s0, c, pk);

@@ -110,10 +110,10 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
       }
     };
     // masks, in step order: bit r = key step_key(r, half) of the chunk lies in this
-    // lane's window (and in the union)
+    // lane's window (and in the union); recomputed when the chunk changes
     int mu = 0, mf = 0;
     uint32_t bits = 0;
-    auto mask = [&](f32x16 (&sc)[1]) {
+    auto prep = [&]() {
       if (mf == 0) {
         bits = 0;
 #pragma unroll
@@ -132,18 +132,20 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
           }
         }
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (!((bits >> r) & 1u)) sc[0][r] = -INFINITY;
       if (++mf == n_frames) {
         mf = 0;
         ++mu;
       }
     };
+    auto mask = [&](f32x16 (&sc)[1]) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (!((bits >> r) & 1u)) sc[0][r] = -INFINITY;
+    };
 
     Block<D> blk[1];
     init_blocks(blk);
-    if (n > 0) run_steps<D, 1, W, true>(n, lds, la, q, blk, p.scale_log2, active, issue, mask);
+    if (n > 0) run_steps<D, 1, W, true>(n, lds, la, q, blk, p.scale_log2, active, issue, prep, mask);
     __syncthreads();   // the ring is reused by the next group of chunk frames
 
     const float l_tot = sum_halves(blk[0].l);
