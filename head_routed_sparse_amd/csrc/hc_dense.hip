@@ -27,7 +27,8 @@ void dense_attn_bf16(const DenseParams p) {
   using R = Ring<D, QB, W>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  __shared__ __attribute__((aligned(1024))) char ring[R::kBytes];
+  constexpr int NS = 4;   // ring stages
+  __shared__ __attribute__((aligned(1024))) char ring[NS * R::kStageBytes];
   lds_char* const lds = (lds_char*)ring;
 
   const int item = xcd_logical(blockIdx.x, p.xcd_group);
@@ -125,7 +126,7 @@ void dense_attn_bf16(const DenseParams p) {
 
   Block<D> blk[QB];
   init_blocks(blk);
-  run_steps<D, QB, W, false>(n, lds, la, q, blk, p.scale_log2, true, issue, [] {}, mask_last);
+  run_steps<D, QB, W, NS, false>(n, lds, la, q, blk, p.scale_log2, true, issue, [] {}, mask_last);
 
   // outputs
 #pragma unroll

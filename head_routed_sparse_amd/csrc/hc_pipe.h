@@ -15,12 +15,12 @@
 namespace hc {
 
 constexpr int kStep = 32;     // keys per pipeline step
-constexpr int kStages = 4;    // LDS ring depth (even: the score buffers alternate with it)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-// Ring geometry for head dim D, QB query blocks per wave and W waves per workgroup.
+// Step-tile geometry for head dim D, QB query blocks per wave and W waves per workgroup
+// (an LDS ring of NS stages takes NS * kStageBytes).
 template <int D, int QB, int W>
 struct Ring {
   static constexpr int kWaves = W;
@@ -30,7 +30,6 @@ struct Ring {
   static constexpr int kStageBytes = 2 * kTileBytes;
   static constexpr int kRowsPerLoad = 1024 / kRowBytes;    // rows one wave-wide 16-B load fills
   static constexpr int kLoads = kStep / kRowsPerLoad / W;  // per wave and tensor
-  static constexpr int kBytes = kStages * kStageBytes;
   static_assert(kLoads >= 1 && kLoads * kRowsPerLoad * W == kStep, "step tile and wave count");
 };
 
@@ -236,20 +235,22 @@ struct LaneAddr {
 //   mask(sc):        edit the scores of the next step before its softmax, without
 //                    branching (called once per step, in order, when kMaskEvery; else
 //                    only for the last step).
-// Step t sits on ring stage (t - r0) mod 4 with r0 = (n - 1) mod 4: the first r0 steps
-// run with run-time stage offsets, the other n - 1 - r0 (a multiple of 4) in groups of
-// four with the offsets folded into the LDS instructions, and the last step lands on
-// stage 0.
+// The ring has NS stages (3 or 4); loads run NS - 1 steps ahead. With G = lcm(2, NS)
+// (the score buffers alternate every step), step t sits on ring stage (t - r0) mod NS
+// with r0 = (n - 1) mod G: the first r0 steps run with run-time stage offsets, the other
+// n - 1 - r0 (a multiple of G) in groups of G with the offsets folded into the LDS
+// instructions, and the last step lands on stage 0 with its scores in the first buffer.
 //   active:          false for a wave with no queries of its own: it still issues its
 //                    share of the loads and meets every barrier, but skips the math.
-template <int D, int QB, int W, bool kMaskEvery, class Issue, class Prep, class Mask>
+template <int D, int QB, int W, int NS, bool kMaskEvery, class Issue, class Prep, class Mask>
 __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D, QB, W>& la,
                                           const u32x4 (&q)[QB][D / 16], Block<D> (&blk)[QB], float c,
                                           bool active, Issue&& issue, Prep&& prep, Mask&& mask) {
   using R = Ring<D, QB, W>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  static_assert(kStages == 4, "the step groups below walk four stages");
+  static_assert(NS == 3 || NS == 4, "ring depth");
+  constexpr int G = NS % 2 == 0 ? NS : 2 * NS;   // steps per group
 
   // S^T of a step for every block (each K fragment read once, used QB times)
   auto scores = [&](f32x16 (&sc)[QB], int stage) {
@@ -279,31 +280,32 @@ __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D
       }
   };
 
-  const int r0 = (n - 1) & 3;
-  // prologue: steps 0 .. kStages-2 in flight, scores of step 0
+  const int r0 = (n - 1) % G;
+  auto stage_of = [&](int t) { return (t - r0 + G) % NS; };   // t >= 0 > -G
+  // prologue: steps 0 .. NS-2 in flight, scores of step 0
 #pragma unroll
-  for (int t = 0; t < kStages - 1; ++t)
-    if (t < n) issue(t, (t - r0) & 3);
-  if (n >= kStages - 1)
-    wait_vmcnt<2 * R::kLoads * (kStages - 2)>();
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < n) issue(t, stage_of(t));
+  if (n >= NS - 1)
+    wait_vmcnt<2 * R::kLoads * (NS - 2)>();
   else
     wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
   f32x16 s0[QB], s1[QB];   // scores of two consecutive steps
-  if (active) scores(s0, (0 - r0) & 3);
+  if (active) scores(s0, stage_of(0));
 
-  // step j on stage `stage` (scores in sc): loads of step j+kStages-1, scores of
-  // step j+1 (into sn) beside the softmax of step j, then PV of step j
+  // step j on stage `stage` (scores in sc): loads of step j+NS-1, scores of step j+1
+  // (into sn) beside the softmax of step j, then PV of step j
   auto step = [&](f32x16 (&sc)[QB], f32x16 (&sn)[QB], int stage, int j) {
-    if (j + kStages - 2 < n)
-      wait_vmcnt<2 * R::kLoads * (kStages - 3)>();
+    if (j + NS - 2 < n)
+      wait_vmcnt<2 * R::kLoads * (NS - 3)>();
     else
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (j + kStages - 1 < n) issue(j + kStages - 1, (stage + kStages - 1) & 3);
+    if (j + NS - 1 < n) issue(j + NS - 1, (stage + NS - 1) % NS);
     if (!active) return;
     if (kMaskEvery) prep();
-    scores(sn, (stage + 1) & 3);
+    scores(sn, (stage + 1) % NS);
     if (kMaskEvery) mask(sc);
     u32x4 pk[QB][2];
     softmax_step(blk, sc, c, pk);
@@ -326,15 +328,19 @@ __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D
 
   int j = 0;
   for (; j < r0; ++j) {
-    step(s0, s1, (j - r0) & 3, j);
+    step(s0, s1, stage_of(j), j);
 #pragma unroll
     for (int b = 0; b < QB; ++b) s0[b] = s1[b];
   }
-  for (; j + 1 < n; j += 4) {
+  for (; j + 1 < n; j += G) {
     step(s0, s1, 0, j);
-    step(s1, s0, 1, j + 1);
-    step(s0, s1, 2, j + 2);
-    step(s1, s0, 3, j + 3);
+    step(s1, s0, 1 % NS, j + 1);
+    step(s0, s1, 2 % NS, j + 2);
+    step(s1, s0, 3 % NS, j + 3);
+    if (G == 6) {
+      step(s0, s1, 4 % NS, j + 4);
+      step(s1, s0, 5 % NS, j + 5);
+    }
   }
   // last step (stage 0, scores in s0)
   if (!active) return;

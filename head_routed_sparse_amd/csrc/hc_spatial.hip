@@ -25,7 +25,8 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
   using R = Ring<D, 1, W>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  __shared__ __attribute__((aligned(1024))) char ring[R::kBytes];
+  constexpr int NS = 4;   // ring stages
+  __shared__ __attribute__((aligned(1024))) char ring[NS * R::kStageBytes];
   lds_char* const lds = (lds_char*)ring;
 
   const SpatialEntry e = p.e[blockIdx.y];
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
 
     Block<D> blk[1];
     init_blocks(blk);
-    if (n > 0) run_steps<D, 1, W, true>(n, lds, la, q, blk, p.scale_log2, active, issue, prep, mask);
+    if (n > 0) run_steps<D, 1, W, NS, true>(n, lds, la, q, blk, p.scale_log2, active, issue, prep, mask);
     __syncthreads();   // the ring is reused by the next group of chunk frames
 
     const float l_tot = sum_halves(blk[0].l);
