@@ -262,6 +262,27 @@ def test_classify_planted_matches_oracle(dtype, d):
         assert np.allclose(stats[h], ref, atol=2e-3), (h, stats[h], ref)
 
 
+def test_max_heads_routed_and_classifier_batches():
+    """The largest head count the ABI takes (64, every class, one dense entry per head)
+    and a classification whose per-head slot entries (12 heads x 8 slots) need more
+    than one dense launch."""
+    g = hin.Geometry(64, 64, 4, 6, 1, 4, 3, 3, "bf16")
+    labels = [S_, D_, P_, G_] * 16
+    inp = hin.generate(g, labels, seed=21)
+    got, _, _ = run_routed(inp)
+    assert_close(got, orc.routed_attention(inp), *TOL["bf16"], what="64 heads")
+    g = hin.Geometry(12, 128, 10, 12, 3, 21, 8, 8, "bf16")
+    labels = [S_, D_, P_, G_, G_, P_, D_, S_, P_, P_, G_, D_]
+    inp = hin.generate(g, labels, seed=22, planted=True)
+    got, stats = classify_gpu(inp, gamma=0.5)
+    want, ost = orc.classify_heads(inp, dict(gamma=0.5))
+    assert list(want) == labels and list(got) == labels
+    for h in range(12):
+        o = ost[h]
+        ref = [o["cos_sink"], o["cos_dummy"], o["cos_spatial"], o["p5"], o["mse"], o["score"]]
+        assert np.allclose(stats[h], ref, atol=2e-3), (h, stats[h], ref)
+
+
 def test_classify_unplanted_statistics_match_oracle():
     g = hin.Geometry(4, 128, 9, 14, 2, 8, 3, 3, "bf16")
     inp = hin.generate(g, [G_] * 4, seed=9)
