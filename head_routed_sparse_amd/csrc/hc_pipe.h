@@ -294,16 +294,20 @@ __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D
   f32x16 s0[QB], s1[QB];   // scores of two consecutive steps
   if (active) scores(s0, stage_of(0));
 
-  // step j on stage `stage` (scores in sc): loads of step j+NS-1, scores of step j+1
-  // (into sn) beside the softmax of step j, then PV of step j
+  // step j on stage `stage` (scores in sc): scores of step j+1 (into sn) beside the
+  // softmax of step j, the loads of step j+NS-1, then PV of step j
   auto step = [&](f32x16 (&sc)[QB], f32x16 (&sn)[QB], int stage, int j) {
     if (j + NS - 2 < n)
       wait_vmcnt<2 * R::kLoads * (NS - 3)>();
     else
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (j + NS - 1 < n) issue(j + NS - 1, (stage + NS - 1) % NS);
-    if (!active) return;
+    // the loads of step j+NS-1 go out just before the PV product (below): issued right
+    // after the barrier, the eight waves of a CU queue on the texture path together
+    if (!active) {
+      if (j + NS - 1 < n) issue(j + NS - 1, (stage + NS - 1) % NS);
+      return;
+    }
     if (kMaskEvery) prep();
     scores(sn, (stage + 1) % NS);
     if (kMaskEvery) mask(sc);
@@ -323,6 +327,7 @@ __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D
       }
       if (i + kAhead < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    if (j + NS - 1 < n) issue(j + NS - 1, (stage + NS - 1) % NS);
     pv(pk, stage);
   };
 
