@@ -217,6 +217,118 @@ def deployed_variants(name, steps, warmup):
     return res
 
 
+# The appendix page's Table 6: LongLive head counts per archetype (Sink, Dummy, Spatial,
+# Global) over its 360 heads at t = 1000, scaled to one 12-head layer and rounded.
+TABLE6_MIX = {"480p": (1.6, 93.8, 168.2, 96.5), "720p": (1.9, 98.2, 167.2, 92.7), "1080p": (1.5, 91.7, 203.2, 63.7)}
+
+
+def table6_labels(name, num_heads):
+    counts = np.array(TABLE6_MIX[name]) * num_heads / 360.0
+    n = np.floor(counts).astype(int)
+    for i in np.argsort(-(counts - n))[: num_heads - n.sum()]:   # largest remainders
+        n[i] += 1
+    return np.repeat(np.arange(4, dtype=np.int32), n)
+
+
+def table6_mix(steps, warmup):
+    """Routed layer-steps with the pages' measured head mix of each resolution
+    (Table 6 of the appendix page) instead of the configs' fixed mix."""
+    import torch
+    from head_routed_sparse_amd import headcast as hc
+    from head_routed_sparse_amd import inputs as hin
+    res = {}
+    for name in ("480p", "720p", "1080p"):
+        inp = hin.config_inputs(name)
+        g = inp.geom
+        dev = lambda a: torch.from_numpy(a).to(torch.bfloat16).cuda()  # noqa: E731
+        q, kh, vh, kc, vc = (dev(a) for a in (inp.q, inp.k_hist, inp.v_hist, inp.k_cur, inp.v_cur))
+        labels = table6_labels(name, g.num_heads)
+        r = {"mix_sink_dummy_spatial_global": [int((labels == c).sum()) for c in range(4)]}
+        for tag, lab in (("routed", labels), ("full_window", np.full(g.num_heads, 3, np.int32))):
+            buf = hc.hc_build_head_buffers(hc.make_desc(g), lab, kh, vh, inp.n_hist_frames)
+            ws = hc.routed_workspace(buf)
+            o = torch.empty_like(q)
+            r[tag + "_ms"] = round(time_calls(lambda: hc.hc_routed_attention(buf, q, kc, vc, out=o, workspace=ws),
+                                              steps, warmup), 4)
+            del buf, ws, o
+        r["speedup_vs_full_window"] = round(r["full_window_ms"] / r["routed_ms"], 3)
+        res[name] = r
+        del inp, q, kh, vh, kc, vc
+    return res
+
+
+def rollout(name, denoise_steps=4, steady_blocks=3):
+    """One layer through an autoregressive rollout: warm-up with every head Global
+    while the window grows (the per-head buffers start empty and take one appended
+    block per step), classification once the window is full at the first denoising
+    step, buffers rebuilt from the monolithic cache, then steady-state steps (routed
+    calls + the append that evicts the oldest rolling block). Random blocks carry no
+    head structure, so the steady state routes with the layer's configured mix; the
+    classification call is timed as the one-time cost it is. denoise_steps per block is
+    a parameter (the pages do not state it)."""
+    import torch
+    from head_routed_sparse_amd import headcast as hc
+    from head_routed_sparse_amd import inputs as hin
+    cfg = hin.CONFIGS[name]
+    g = cfg["geom"]
+    C, S, H, d = g.chunk_frames, g.tokens_per_frame, g.num_heads, g.head_dim
+    desc = hc.make_desc(g)
+    gen = torch.Generator(device="cuda").manual_seed(4242)
+    blk = lambda: torch.randn(3, C * S, H, d, device="cuda", generator=gen).to(torch.bfloat16)  # noqa: E731
+    n_warm = g.window_frames // C - 1        # blocks stored before the window is full
+    all_global = np.full(H, 3, np.int32)
+    buf = hc.hc_build_head_buffers(desc, all_global, None, None, 0)
+    ws = hc.routed_workspace(buf)
+    mono_k, mono_v = [], []
+    warm_ms = []
+    for _ in range(n_warm):
+        q, k, v = blk()
+        o = torch.empty_like(q)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(denoise_steps):
+            hc.hc_routed_attention(buf, q, k, v, out=o, workspace=ws)
+        hc.hc_append_chunk(buf, k, v)
+        torch.cuda.synchronize()
+        warm_ms.append(round((time.perf_counter() - t0) * 1e3, 3))
+        mono_k.append(k)
+        mono_v.append(v)
+    kh, vh = torch.cat(mono_k), torch.cat(mono_v)
+    q, k, v = blk()
+    params = hc.hc_default_classify_params()
+    cws = torch.empty(hc.hc_classify_workspace_bytes(desc, params, g.hist_frames), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    labels, _ = hc.hc_classify_heads(desc, params, q, kh, vh, g.hist_frames, k, v, workspace=cws)
+    classify_ms = (time.perf_counter() - t0) * 1e3
+    out = {"workload": f"{name} one layer, {denoise_steps} denoising steps per block",
+           "warmup_ms_per_ar_step": warm_ms, "classify_ms": round(classify_ms, 3),
+           "classified_labels_on_random_blocks": [int((labels == c).sum()) for c in range(4)]}
+    for tag, lab in (("routed", cfg["labels"]), ("full_window", all_global)):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        b = hc.hc_build_head_buffers(desc, lab, kh, vh, g.hist_frames)
+        torch.cuda.synchronize()
+        out[tag + "_build_ms"] = round((time.perf_counter() - t0) * 1e3, 3)
+        w = hc.routed_workspace(b)
+        steps_ms = []
+        for _ in range(steady_blocks + 1):
+            q, k, v = blk()
+            o = torch.empty_like(q)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(denoise_steps):
+                hc.hc_routed_attention(b, q, k, v, out=o, workspace=w)
+            hc.hc_append_chunk(b, k, v)
+            torch.cuda.synchronize()
+            steps_ms.append((time.perf_counter() - t0) * 1e3)
+        out[tag + "_ms_per_ar_step"] = round(float(np.median(steps_ms[1:])), 3)
+        del b, w
+    out["steady_speedup"] = round(out["full_window_ms_per_ar_step"] / out["routed_ms_per_ar_step"], 3)
+    out["classify_in_steady_ar_steps"] = round(out["classify_ms"] / out["routed_ms_per_ar_step"], 2)
+    return out
+
+
 def full_step(steps, warmup):
     """The 30-layer 720P step with planted heads: classify every layer once (labels
     must equal the planted ones), build its buffers, then time one denoise step =
@@ -363,6 +475,21 @@ def main():
                                          (sec["routed"]["kernels"]["dense"][0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "classify_ms": round(sec["classify_ms"], 3)}
         del sec
+    print("[bench] third workload 480p", file=sys.stderr, flush=True)
+    th = measure("480p", max(3, a.steps // 2), 2, with_events=True)
+    gt = th["geom"]
+    out["third_workload"] = {
+        "workload": "480p", "routed_ms": round(th["routed"]["ms"], 4),
+        "full_window_ms": round(th["all_global"]["ms"], 4),
+        "speedup_vs_full_window": round(th["all_global"]["ms"] / th["routed"]["ms"], 3),
+        "dense_roofline_frac": round(dense_flops(gt, th["routed"]["labels"], gt.hist_frames) /
+                                     (th["routed"]["kernels"]["dense"][0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "classify_ms": round(th["classify_ms"], 3)}
+    del th
+    print("[bench] table-6 head mixes", file=sys.stderr, flush=True)
+    out["table6_mix"] = table6_mix(max(3, a.steps // 4), 2)
+    print("[bench] rollout", file=sys.stderr, flush=True)
+    out["rollout_720p"] = rollout("720p")
     print("[bench] deployed path variants", file=sys.stderr, flush=True)
     out["deployed_variants"] = {n: deployed_variants(n, max(3, a.steps // 4), 2) for n in ("720p", "1080p")}
     print("[bench] table-4 style ablation", file=sys.stderr, flush=True)
