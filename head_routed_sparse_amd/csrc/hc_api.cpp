@@ -274,13 +274,14 @@ struct hc_head_buffers {
   std::vector<int64_t> head_off;     // element offset of head rows in a region, -1 = none
   std::vector<int64_t> head_rows;    // row capacity
   int64_t next_block = 0;
-  // routed plan (rebuilt when the ring fill changes)
+  // routed plan (rebuilt only when some head's stored history length changes)
   int64_t plan_block = -1;
+  std::vector<int32_t> plan_hist_len;
   std::vector<Entry> entries;
   std::vector<MergeEntry> merges;
   std::vector<SpatialEntry> spatials;
   int n_slots = 0;
-  int max_slots = 0;
+  int max_slots = -1;               // partial slots the routed workspace provides
   bool plan_only = false;            // host-only handle (hc_plan_head_buffers)
 };
 
@@ -338,6 +339,16 @@ void build_plan(hc_head_buffers* b) {
     plan_splits(es, nqt);
     return es;
   };
+  // the plan depends on the state only through the stored history lengths, which stop
+  // changing once the window is full: steady-state appends keep the plan
+  std::vector<int32_t> hist_len(d.num_heads);
+  for (int h = 0; h < d.num_heads; ++h)
+    hist_len[h] = (int32_t)(stored_frames(d, b->labels[h], b->next_block) * S);
+  if (b->plan_block >= 0 && hist_len == b->plan_hist_len) {
+    b->plan_block = b->next_block;
+    return;
+  }
+  b->plan_hist_len = hist_len;
   std::vector<Entry> es = make(b->next_block);
   // slots: split heads and Spatial heads write fp32 partials
   int slot = 0;
@@ -374,14 +385,17 @@ void build_plan(hc_head_buffers* b) {
   b->entries = es;
   b->n_slots = slot;
   b->plan_block = b->next_block;
-  // workspace sized for the full ring (the most slots any fill state needs)
-  std::vector<Entry> full = make(1 + rolling_blocks(d));
-  int ms = 0;
-  for (const Entry& e : full) {
-    const int cls = b->labels[e.head];
-    ms += (cls == HC_SPATIAL && !spatial_cells(d)) ? 1 : (e.nsplit > 1 ? e.nsplit : 0);
+  // workspace sized for the full ring (the most slots any fill state needs), once
+  if (b->max_slots < 0) {
+    std::vector<Entry> full = make(1 + rolling_blocks(d));
+    int ms = 0;
+    for (const Entry& e : full) {
+      const int cls = b->labels[e.head];
+      ms += (cls == HC_SPATIAL && !spatial_cells(d)) ? 1 : (e.nsplit > 1 ? e.nsplit : 0);
+    }
+    b->max_slots = ms;
   }
-  b->max_slots = std::max(ms, slot);
+  b->max_slots = std::max(b->max_slots, slot);
 }
 
 size_t partial_bytes(int slots, int64_t lq, int head_dim) {
