@@ -152,6 +152,22 @@ def measure(name, steps, warmup, with_events, only_routed=False, labels_override
                                                                   memory=mem), 3, 1)
     buf = hc.hc_build_head_buffers(desc, inp.labels, kh, vh, inp.n_hist_frames, memory=mem)
     res["append_ms"] = time_calls(lambda: hc.hc_append_chunk(buf, kc, vc), 6, 2)
+    # copy-kernel durations (HIP events on the library's stream) of one build and one append
+    hc.hc_timing_read()
+    hc.hc_timing_enable(True)
+    hc.hc_build_head_buffers(desc, inp.labels, kh, vh, inp.n_hist_frames, memory=mem)
+    res["build_kernel_ms"] = hc.hc_timing_read()["copy"][0]
+    hc.hc_append_chunk(buf, kc, vc)
+    res["append_kernel_ms"] = hc.hc_timing_read()["copy"][0]
+    hc.hc_timing_enable(False)
+    # bytes the copies move (read + write, K and V): every stored history row of the
+    # routed heads once; for an append, the heads that take the block
+    S, C = g.tokens_per_frame, g.chunk_frames
+    row = 2 * 2 * g.head_dim * 2
+    lab = np.asarray(inp.labels)
+    stored = {0: C, 1: 0, 2: g.hist_frames, 3: g.hist_frames}
+    res["build_bytes"] = int(sum(stored[int(c)] for c in lab) * S * row)
+    res["append_bytes"] = int(np.isin(lab, (2, 3)).sum() * C * S * row)
     p = hc_default_classify_params(gamma=0.5)
     ws = torch.empty(hc.hc_classify_workspace_bytes(desc, p, inp.n_hist_frames), dtype=torch.uint8, device="cuda")
     res["classify_ms"] = time_calls(lambda: hc.hc_classify_heads(desc, p, q, kh, vh, inp.n_hist_frames, kc, vc,
@@ -457,6 +473,12 @@ def main():
                            "avg_ms": round(r["kernels"].get("spatial", (0, 0))[0], 4),
                            "hbm_frac": round(sp_bytes / (r["kernels"]["spatial"][0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
                            if "spatial" in r["kernels"] else None},
+        "copies": {"build_bytes": main_res["build_bytes"], "build_kernel_ms": round(main_res["build_kernel_ms"], 4),
+                   "build_hbm_frac": round(main_res["build_bytes"] / (main_res["build_kernel_ms"] * 1e-3) / 1e9 /
+                                           PEAK_HBM_GBS, 4),
+                   "append_bytes": main_res["append_bytes"], "append_kernel_ms": round(main_res["append_kernel_ms"], 4),
+                   "append_hbm_frac": round(main_res["append_bytes"] / (main_res["append_kernel_ms"] * 1e-3) / 1e9 /
+                                            PEAK_HBM_GBS, 4)},
         "one_time_ms": {"build_buffers": round(main_res["build_ms"], 3), "append_chunk": round(main_res["append_ms"], 3),
                         "classify_heads": round(main_res["classify_ms"], 3)},
         "kv_cache_bytes": {"per_head_buffers": main_res["kv_bytes_routed"],

@@ -7,7 +7,7 @@
 namespace hc {
 
 constexpr int kMaxEntries = 64;   // dense work entries per launch (kernel arguments by value)
-constexpr int kKeyTile = 64;      // keys per LDS tile in the dense and spatial kernels
+constexpr int kKeyTile = 64;      // granularity of key-range splits (a multiple of the 32-key step)
 constexpr int kDenseQ = 128;      // queries per dense workgroup (query tile)
 constexpr int kXcdGroup = 8;      // consecutive items (same key range) kept on one XCD
 constexpr int kSpTileR = 4;       // Spatial query tile: 4 rows x 8 cols of positions
