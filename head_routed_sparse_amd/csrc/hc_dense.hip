@@ -126,7 +126,12 @@ void dense_attn_bf16(const DenseParams p) {
 
   Block<D> blk[QB];
   init_blocks(blk);
-  run_steps<D, QB, W, NS, false>(n, lds, la, q, blk, p.scale_log2, true, issue, [] {}, mask_last);
+  const float c = p.scale_log2;
+  auto soft = [&](f32x16 (&sc)[QB], u32x4 (&pk)[QB][2], bool last) {
+    if (last) mask_last(sc);
+    softmax_step(blk, sc, c, pk);
+  };
+  run_steps<D, QB, W, NS>(n, lds, la, q, blk, true, issue, [] {}, soft);
 
   // outputs
 #pragma unroll

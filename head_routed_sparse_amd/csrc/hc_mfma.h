@@ -88,4 +88,12 @@ __device__ __forceinline__ int xcd_logical(int bid, int group) {
   return base + (within % 8) * group + within / 8;
 }
 
+// Workgroup id -> logical index in [0, total) such that the workgroups of one XCD
+// (ids x, x + 8, x + 16, ...) take one contiguous block of logical indices.
+__device__ __forceinline__ int xcd_block(int bid, int total) {
+  const int x = bid & 7, k = bid >> 3;
+  const int q = total >> 3, r = total & 7;
+  return x * q + min(x, r) + k;
+}
+
 }  // namespace hc

@@ -108,21 +108,35 @@ __device__ __forceinline__ float step_max(const f32x16& s) {
   return max_halves(m);
 }
 
-// p = exp2(s c - m) packed to bf16 pairs (register r of the scores = element r of the
-// B operand of the PV product); returns this lane's sum of the same rounded p.
-__device__ __forceinline__ float exponentiate(const f32x16& s, float m, float c, u32x4 (&pk)[2]) {
+// p = exp2(s c + add(r)) packed to bf16 pairs (register r of the scores = element r of
+// the B operand of the PV product); returns this lane's sum of the same rounded p. The
+// addend is -m, or -inf for a key the query does not see (p = 0 exactly).
+template <class Add>
+__device__ __forceinline__ float exponentiate(const f32x16& s, Add&& add, float c, u32x4 (&pk)[2]) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
   float ls = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float p0 = fast_exp2(__builtin_fmaf(s[2 * e], c, -m));
-    const float p1 = fast_exp2(__builtin_fmaf(s[2 * e + 1], c, -m));
+    const float p0 = fast_exp2(__builtin_fmaf(s[2 * e], c, add(2 * e)));
+    const float p1 = fast_exp2(__builtin_fmaf(s[2 * e + 1], c, add(2 * e + 1)));
     const uint32_t w = pack_bf16(p0, p1);
     pk[e >> 2][e & 3] = w;
     ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, ls, false);
   }
   return ls;
+}
+
+// Move the reference max of a block to m_new (>= m): rescale O and l.
+template <int D>
+__device__ __forceinline__ void move_max(Block<D>& b, float m_new) {
+  const float f = fast_exp2(b.m - m_new);
+  b.l *= f;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) b.o[db][r] *= f;
+  b.m = m_new;
 }
 
 // Softmax of one step for every block: exponentiate against the reference max; in
@@ -135,21 +149,16 @@ __device__ __forceinline__ void softmax_step(Block<D> (&blk)[QB], const f32x16 (
   bool over = false;
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
-    ls[b] = exponentiate(sc[b], blk[b].m, c, pk[b]);
+    const float neg_m = -blk[b].m;
+    ls[b] = exponentiate(sc[b], [&](int) { return neg_m; }, c, pk[b]);
     over |= ls[b] > kSumLimit;
   }
   if (__builtin_amdgcn_ballot_w64(over)) {
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
-      const float m_new = __builtin_fmaxf(blk[b].m, step_max(sc[b]) * c);
-      const float f = fast_exp2(blk[b].m - m_new);
-      blk[b].l *= f;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) blk[b].o[db][r] *= f;
-      blk[b].m = m_new;
-      ls[b] = exponentiate(sc[b], m_new, c, pk[b]);
+      move_max(blk[b], __builtin_fmaxf(blk[b].m, step_max(sc[b]) * c));
+      const float neg_m = -blk[b].m;
+      ls[b] = exponentiate(sc[b], [&](int) { return neg_m; }, c, pk[b]);
     }
   }
 #pragma unroll
@@ -230,11 +239,11 @@ struct LaneAddr {
 // The step pipeline over n >= 1 steps of 32 keys for W waves of QB query blocks.
 //   issue(t, stage): start the direct loads of step t into ring stage `stage` (called
 //                    once for t = 0, 1, 2, ... in order);
-//   prep():          get ready to mask the next step (may branch; called once per step,
-//                    in order, before that step's score MFMAs are issued, when kMaskEvery);
-//   mask(sc):        edit the scores of the next step before its softmax, without
-//                    branching (called once per step, in order, when kMaskEvery; else
-//                    only for the last step).
+//   prep():          get ready for the softmax of the next step (may branch; called once
+//                    per step, in order, before the score MFMAs issued beside it);
+//   soft(sc, pk, last): the softmax of that step: fold its scores sc into the blocks'
+//                    running max and sum and write the bf16 probabilities to pk (last is
+//                    true for the final step only).
 // The ring has NS stages (3 or 4); loads run NS - 1 steps ahead. With G = lcm(2, NS)
 // (the score buffers alternate every step), step t sits on ring stage (t - r0) mod NS
 // with r0 = (n - 1) mod G: the first r0 steps run with run-time stage offsets, the other
@@ -242,10 +251,10 @@ struct LaneAddr {
 // instructions, and the last step lands on stage 0 with its scores in the first buffer.
 //   active:          false for a wave with no queries of its own: it still issues its
 //                    share of the loads and meets every barrier, but skips the math.
-template <int D, int QB, int W, int NS, bool kMaskEvery, class Issue, class Prep, class Mask>
+template <int D, int QB, int W, int NS, class Issue, class Prep, class Soft>
 __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D, QB, W>& la,
-                                          const u32x4 (&q)[QB][D / 16], Block<D> (&blk)[QB], float c,
-                                          bool active, Issue&& issue, Prep&& prep, Mask&& mask) {
+                                          const u32x4 (&q)[QB][D / 16], Block<D> (&blk)[QB], bool active,
+                                          Issue&& issue, Prep&& prep, Soft&& soft) {
   using R = Ring<D, QB, W>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -308,11 +317,10 @@ __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D
       if (j + NS - 1 < n) issue(j + NS - 1, (stage + NS - 1) % NS);
       return;
     }
-    if (kMaskEvery) prep();
+    prep();
     scores(sn, (stage + 1) % NS);
-    if (kMaskEvery) mask(sc);
     u32x4 pk[QB][2];
-    softmax_step(blk, sc, c, pk);
+    soft(sc, pk, false);
     // issue in order: alternate each score MFMA with the exponentials that fit under
     // it, and read K fragments kAhead MFMA groups ahead of their use
     constexpr int kAhead = 3;
@@ -349,10 +357,9 @@ __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D
   }
   // last step (stage 0, scores in s0)
   if (!active) return;
-  if (kMaskEvery) prep();
-  mask(s0);
+  prep();
   u32x4 pk[QB][2];
-  softmax_step(blk, s0, c, pk);
+  soft(s0, pk, true);
   pv(pk, 0);
 }
 

@@ -29,8 +29,12 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
   __shared__ __attribute__((aligned(1024))) char ring[NS * R::kStageBytes];
   lds_char* const lds = (lds_char*)ring;
 
-  const SpatialEntry e = p.e[blockIdx.y];
-  const int tr = blockIdx.x / p.tiles_c, tc = blockIdx.x % p.tiles_c;
+  // the tiles of one XCD are neighbours, so the L2 keeps the window rows they share
+  const int n_tiles = p.tiles_r * p.tiles_c;
+  const int lid = xcd_block(blockIdx.x, n_tiles * p.n_entries);
+  const SpatialEntry e = p.e[lid / n_tiles];
+  const int tile = lid % n_tiles;
+  const int tr = tile / p.tiles_c, tc = tile % p.tiles_c;
   const int fh = p.frame_h, fw = p.frame_w, S = fh * fw;
   const bool cells = p.cells != 0;
   // window of a position: sliding g x g (never cut) or its own cell
@@ -110,10 +114,20 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
         ++iu;
       }
     };
-    // masks, in step order: bit r = key step_key(r, half) of the chunk lies in this
-    // lane's window (and in the union); recomputed when the chunk changes
+    Block<D> blk[1];
+    init_blocks(blk);
+    const float c = p.scale_log2;
+    // window of this lane's query over the keys of the current union chunk: bit r =
+    // key step_key(r, half) lies in the window (and in the union). The exponent addends
+    // are -m inside, -inf outside, so masking costs nothing per step; they change with
+    // the chunk and with the reference max.
     int mu = 0, mf = 0;
     uint32_t bits = 0;
+    float add[16];
+    auto refresh = [&]() {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) add[r] = (bits >> r) & 1u ? -blk[0].m : -INFINITY;
+    };
     auto prep = [&]() {
       if (mf == 0) {
         bits = 0;
@@ -132,21 +146,28 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
             }
           }
         }
+        refresh();
       }
       if (++mf == n_frames) {
         mf = 0;
         ++mu;
       }
     };
-    auto mask = [&](f32x16 (&sc)[1]) {
+    auto soft = [&](f32x16 (&sc)[1], u32x4 (&pk)[1][2], bool) {
+      float ls = exponentiate(sc[0], [&](int r) { return add[r]; }, c, pk[0]);
+      if (__builtin_amdgcn_ballot_w64(ls > kSumLimit)) {   // move the reference max
+        float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (!((bits >> r) & 1u)) sc[0][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r)
+          if ((bits >> r) & 1u) mx = __builtin_fmaxf(mx, sc[0][r]);
+        move_max(blk[0], __builtin_fmaxf(blk[0].m, max_halves(mx) * c));
+        refresh();
+        ls = exponentiate(sc[0], [&](int r) { return add[r]; }, c, pk[0]);
+      }
+      blk[0].l += ls;
     };
 
-    Block<D> blk[1];
-    init_blocks(blk);
-    if (n > 0) run_steps<D, 1, W, NS, true>(n, lds, la, q, blk, p.scale_log2, active, issue, prep, mask);
+    if (n > 0) run_steps<D, 1, W, NS>(n, lds, la, q, blk, active, issue, prep, soft);
     __syncthreads();   // the ring is reused by the next group of chunk frames
 
     const float l_tot = sum_halves(blk[0].l);
@@ -201,7 +222,7 @@ hipError_t launch_spatial_f32(const SpatialParams& p, int head_dim, hipStream_t 
 hipError_t launch_spatial(const SpatialParams& p, int head_dim, int bf16, hipStream_t s) {
   if (p.n_entries == 0) return hipSuccess;
   if (!bf16) return launch_spatial_f32(p, head_dim, s);
-  const dim3 grid(p.tiles_r * p.tiles_c, p.n_entries), block(256);
+  const dim3 grid(p.tiles_r * p.tiles_c * p.n_entries), block(256);
   if (head_dim == 128)
     hipLaunchKernelGGL(spatial_attn_bf16<128>, grid, block, 0, s, p);
   else
