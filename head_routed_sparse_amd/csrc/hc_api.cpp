@@ -6,12 +6,14 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <functional>
+#include <map>
 #include <mutex>
 #include <queue>
 #include <string>
@@ -216,6 +218,67 @@ void plan_splits(std::vector<Entry>& es, int nqt) {
   }
 }
 
+// Spatial query tile (tile_r x tile_c positions, 24..32 of them): the shape with the
+// shortest estimated Spatial kernel. A tile costs one step per 32 keys of the union of
+// its positions' windows (per frame); the tiles of all heads are list-scheduled,
+// longest first, on kNumCu * kSlotsPerCu workgroup slots. Ties go to the fewer steps.
+// Results are kept per geometry (the search takes milliseconds).
+void choose_spatial_tile(int fh, int fw, int gh, int gw, bool cells, int n_heads, int* tile_r, int* tile_c) {
+  static std::mutex mu;
+  static std::map<std::array<int, 6>, std::pair<int, int>> memo;
+  const std::array<int, 6> key{fh, fw, gh, gw, cells ? 1 : 0, n_heads};
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = memo.find(key);
+    if (it != memo.end()) {
+      *tile_r = it->second.first;
+      *tile_c = it->second.second;
+      return;
+    }
+  }
+  auto lo = [&](int pos, int g, int ext) { return cells ? cell_origin(pos, g) : win_origin(pos, g, ext); };
+  auto hi = [&](int pos, int g, int ext) {
+    return lo(pos, g, ext) + (cells ? cell_extent(pos, g, ext) : std::min(g, ext));
+  };
+  double best_t = -1.0;
+  int64_t best_total = 0;
+  *tile_r = 4;
+  *tile_c = 8;
+  std::vector<int> steps;
+  for (int a = 1; a <= kSpTileMax; ++a)
+    for (int b = 1; a * b <= kSpTileMax; ++b) {
+      if (4 * a * b < 3 * kSpTileMax) continue;   // keep >= 3/4 of the MFMA rows busy
+      if (a > fh || b > fw) continue;             // (no candidate: a frame under 24 positions keeps 4 x 8)
+      steps.clear();
+      for (int r0 = 0; r0 < fh; r0 += a)
+        for (int c0 = 0; c0 < fw; c0 += b) {
+          const int r1 = std::min(r0 + a, fh) - 1, c1 = std::min(c0 + b, fw) - 1;
+          const int ur = hi(r1, gh, fh) - lo(r0, gh, fh), uc = hi(c1, gw, fw) - lo(c0, gw, fw);
+          steps.push_back(ceil_div((int64_t)ur * uc, 32));
+        }
+      std::sort(steps.begin(), steps.end(), std::greater<int>());
+      std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> slots;
+      for (int i = 0; i < kNumCu * kSlotsPerCu; ++i) slots.push(0);
+      int64_t span = 0, total = 0;
+      for (int st : steps)
+        for (int h = 0; h < n_heads; ++h) {
+          const int64_t t = slots.top() + st;
+          slots.pop();
+          slots.push(t);
+          span = std::max(span, t);
+          total += st;
+        }
+      if (best_t < 0 || span < best_t || (span == best_t && total < best_total)) {
+        best_t = (double)span;
+        best_total = total;
+        *tile_r = a;
+        *tile_c = b;
+      }
+    }
+  std::lock_guard<std::mutex> lk(mu);
+  memo[key] = {*tile_r, *tile_c};
+}
+
 // Items of one key range (its query tiles) are dispatched consecutively; keeping a
 // run of them on one XCD lets them share the key range through that XCD's L2.
 int xcd_group_size(int nqt) {
@@ -280,6 +343,7 @@ struct hc_head_buffers {
   std::vector<Entry> entries;
   std::vector<MergeEntry> merges;
   std::vector<SpatialEntry> spatials;
+  int sp_tile_r = 0, sp_tile_c = 0;   // Spatial query tile
   int n_slots = 0;
   int max_slots = -1;               // partial slots the routed workspace provides
   bool plan_only = false;            // host-only handle (hc_plan_head_buffers)
@@ -382,6 +446,9 @@ void build_plan(hc_head_buffers* b) {
       slot += e.nsplit;
     }
   }
+  if (!b->spatials.empty() && b->sp_tile_r == 0)
+    choose_spatial_tile(d.frame_h, d.frame_w, d.grid_h, d.grid_w, spatial_cells(d), (int)b->spatials.size(),
+                        &b->sp_tile_r, &b->sp_tile_c);
   b->entries = es;
   b->n_slots = slot;
   b->plan_block = b->next_block;
@@ -649,8 +716,10 @@ hc_status hc_routed_attention(const hc_head_buffers* b, const void* q, const voi
     sp.n_hist_frames = (int)stored_frames(d, HC_SPATIAL, b->next_block);
     sp.grid_h = d.grid_h;
     sp.grid_w = d.grid_w;
-    sp.tiles_r = ceil_div(d.frame_h, kSpTileR);
-    sp.tiles_c = ceil_div(d.frame_w, kSpTileC);
+    sp.tile_r = b->sp_tile_r;
+    sp.tile_c = b->sp_tile_c;
+    sp.tiles_r = ceil_div(d.frame_h, sp.tile_r);
+    sp.tiles_c = ceil_div(d.frame_w, sp.tile_c);
     sp.scale_log2 = p.scale_log2;
     sp.cells = spatial_cells(d) ? 1 : 0;
     sp.k_cur = k_cur;
@@ -825,8 +894,9 @@ hc_status hc_classify_heads(const hc_layer_desc* desc, const hc_classify_params*
   sp.n_hist_frames = n_hist_frames;
   sp.grid_h = params->proxy_grid_h > 0 ? params->proxy_grid_h : d.grid_h;
   sp.grid_w = params->proxy_grid_w > 0 ? params->proxy_grid_w : d.grid_w;
-  sp.tiles_r = ceil_div(d.frame_h, kSpTileR);
-  sp.tiles_c = ceil_div(d.frame_w, kSpTileC);
+  choose_spatial_tile(d.frame_h, d.frame_w, sp.grid_h, sp.grid_w, false, H, &sp.tile_r, &sp.tile_c);
+  sp.tiles_r = ceil_div(d.frame_h, sp.tile_r);
+  sp.tiles_c = ceil_div(d.frame_w, sp.tile_c);
   sp.scale_log2 = p.scale_log2;
   for (int h0 = 0; h0 < H; h0 += kMaxEntries) {
     const int n = std::min(H - h0, kMaxEntries);

@@ -10,8 +10,24 @@ constexpr int kMaxEntries = 64;   // dense work entries per launch (kernel argum
 constexpr int kKeyTile = 64;      // granularity of key-range splits (a multiple of the 32-key step)
 constexpr int kDenseQ = 128;      // queries per dense workgroup (query tile)
 constexpr int kXcdGroup = 8;      // consecutive items (same key range) kept on one XCD
-constexpr int kSpTileR = 4;       // Spatial query tile: 4 rows x 8 cols of positions
-constexpr int kSpTileC = 8;
+constexpr int kSpTileMax = 32;    // positions per Spatial query tile (one 32-query MFMA block)
+
+// First row (or column) of the g-wide Spatial window around pos in a frame of `extent`
+// rows (columns): the query sits at offset g/2, and the window is shifted (never cut)
+// to stay inside the frame; g >= extent covers the whole frame.
+__host__ __device__ __forceinline__ int win_origin(int pos, int g, int extent) {
+  const int o = pos - g / 2;
+  const int hi = extent - g > 0 ? extent - g : 0;
+  return o < 0 ? 0 : (o > hi ? hi : o);
+}
+
+// Non-overlapping cells: origin and size of the cell holding pos (the last cell keeps
+// the remainder rows / columns).
+__host__ __device__ __forceinline__ int cell_origin(int pos, int cell) { return (pos / cell) * cell; }
+__host__ __device__ __forceinline__ int cell_extent(int pos, int cell, int extent) {
+  const int o = cell_origin(pos, cell);
+  return cell < extent - o ? cell : extent - o;
+}
 
 // One dense work entry: a head's queries against one contiguous key range made of
 // [history rows 0..hist_len) followed by [current-block rows 0..cur_len). The range is
@@ -92,6 +108,7 @@ struct SpatialParams {
   int32_t frame_h, frame_w, chunk_frames;
   int32_t n_hist_frames;   // valid history frames (a prefix of the buffer positions)
   int32_t grid_h, grid_w;
+  int32_t tile_r, tile_c;    // query tile: rows x cols of positions (tile_r * tile_c <= kSpTileMax)
   int32_t tiles_r, tiles_c;  // position tiles per frame
   int32_t n_entries;
   float scale_log2;

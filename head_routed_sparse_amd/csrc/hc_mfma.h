@@ -61,23 +61,6 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);   // a.hi | b.hi << 16
 }
 
-// First row (or column) of the g-wide Spatial window around pos in a frame of `extent`
-// rows (columns): the query sits at offset g/2, and the window is shifted (never cut)
-// to stay inside the frame; g >= extent covers the whole frame.
-__host__ __device__ __forceinline__ int win_origin(int pos, int g, int extent) {
-  const int o = pos - g / 2;
-  const int hi = extent - g > 0 ? extent - g : 0;
-  return o < 0 ? 0 : (o > hi ? hi : o);
-}
-
-// Non-overlapping cells: origin and size of the cell holding pos (the last cell keeps
-// the remainder rows / columns).
-__host__ __device__ __forceinline__ int cell_origin(int pos, int cell) { return (pos / cell) * cell; }
-__host__ __device__ __forceinline__ int cell_extent(int pos, int cell, int extent) {
-  const int o = cell_origin(pos, cell);
-  return cell < extent - o ? cell : extent - o;
-}
-
 // Work item -> logical index, keeping runs of kXcdGroup consecutive logical items on
 // one XCD (workgroups are dispatched round-robin over the 8 XCDs) while the overall
 // dispatch order still follows the logical order.

@@ -3,10 +3,10 @@
 // query (f, r, c) of the current block attends, in each history frame, to the g x g
 // window whose origin is clamp(r - g/2, 0, fh - g) x clamp(c - g/2, 0, fw - g).
 //
-// A workgroup (4 waves) takes a tile of 4 x 8 positions of one Spatial head, one wave
-// per chunk frame (the chunk frames at one position share the key set exactly; with
-// three chunk frames the fourth wave only loads). It walks the union of the 32
-// windows in 32-key steps, chunk-outer and frame-inner, on the dense kernel's pipeline
+// A workgroup (4 waves) takes a tile of up to 32 positions (tile_r x tile_c, chosen by
+// the host) of one Spatial head, one wave per chunk frame (the chunk frames at one
+// position share the key set exactly; with three chunk frames the fourth wave only
+// loads). It walks the union of the tile's windows in 32-key steps, chunk-outer and frame-inner, on the dense kernel's pipeline
 // (hc_pipe.h): every step's rows are gathered whole (256 B) by 16-byte direct loads
 // into the LDS ring, and keys outside a query's own window are masked. The union
 // position of every row a lane loads, and every lane's mask bits, depend only on the
@@ -42,8 +42,8 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
   auto org_c = [&](int c) { return cells ? cell_origin(c, p.grid_w) : win_origin(c, p.grid_w, fw); };
   auto ext_r = [&](int r) { return cells ? cell_extent(r, p.grid_h, fh) : min(p.grid_h, fh); };
   auto ext_c = [&](int c) { return cells ? cell_extent(c, p.grid_w, fw) : min(p.grid_w, fw); };
-  const int R0 = tr * kSpTileR, C0 = tc * kSpTileC;
-  const int R1 = min(R0 + kSpTileR, fh) - 1, C1 = min(C0 + kSpTileC, fw) - 1;
+  const int R0 = tr * p.tile_r, C0 = tc * p.tile_c;
+  const int R1 = min(R0 + p.tile_r, fh) - 1, C1 = min(C0 + p.tile_c, fw) - 1;
   // union of the windows of the tile's positions (origins and ends grow with the position)
   const int ur0 = org_r(R0), ur1 = org_r(R1) + ext_r(R1);
   const int uc0 = org_c(C0), uc1 = org_c(C1) + ext_c(C1);
@@ -60,8 +60,8 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int half = lane >> 5;
-  const int pr = R0 + l32 / kSpTileC, pc = C0 + l32 % kSpTileC;
-  const bool pos_ok = pr < fh && pc < fw;
+  const int pr = R0 + l32 / p.tile_c, pc = C0 + l32 % p.tile_c;
+  const bool pos_ok = l32 < p.tile_r * p.tile_c && pr < fh && pc < fw;
   const int r0q = org_r(min(pr, fh - 1)), ehq = ext_r(min(pr, fh - 1));
   const int c0q = org_c(min(pc, fw - 1)), ewq = ext_c(min(pc, fw - 1));
 
