@@ -129,16 +129,22 @@ def measure(name, steps, warmup, with_events, only_routed=False, labels_override
         if with_events:
             hc.hc_timing_read()
             hc.hc_timing_enable(True)
+        # per-call durations from events on the call's stream (median and min beside the mean)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         t0 = time.perf_counter()
-        for _ in range(steps):
+        for e0, e1 in evs:
+            e0.record()
             fn()
+            e1.record()
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / steps
+        call_ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
         kern = {}
         if with_events:
             hc.hc_timing_enable(False)
             kern = {k: (v[0] / max(v[1], 1), v[1]) for k, v in hc.hc_timing_read().items() if v[1]}
-        res[tag] = dict(ms=ms, kernels=kern, labels=labels)
+        res[tag] = dict(ms=ms, kernels=kern, labels=labels, call_median=float(np.median(call_ms)),
+                        call_min=float(call_ms.min()))
         del buf, ws, out
     res["geom"] = g
     res["inp"] = inp
@@ -462,6 +468,10 @@ def main():
                    "global_batch": 1, "seq_len": g.lq, "parallelism": "none (1 GPU)"},
         "speedup_vs_full_window": round(base["ms"] / r["ms"], 3),
         "full_window_ms": round(base["ms"], 4),
+        "per_call_ms": {"routed_median": round(r["call_median"], 4), "routed_min": round(r["call_min"], 4),
+                        "full_window_median": round(base["call_median"], 4),
+                        "full_window_min": round(base["call_min"], 4),
+                        "infinity_cache_flushed": False},
         "kernel_avg_ms": {k: round(v[0], 4) for k, v in r["kernels"].items()},
         "full_window_kernel_avg_ms": {k: round(v[0], 4) for k, v in base["kernels"].items()},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
