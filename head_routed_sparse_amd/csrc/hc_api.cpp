@@ -279,6 +279,18 @@ void choose_spatial_tile(int fh, int fw, int gh, int gw, bool cells, int n_heads
   memo[key] = {*tile_r, *tile_c};
 }
 
+// Frame parts of the Spatial launch: when the tiles of all Spatial heads leave
+// workgroup slots free, each tile's frames are split over that many workgroups (their
+// partials are merged afterwards), shortening the chain of dependent steps. bf16 only;
+// at most kMaxSpParts and one frame per part.
+constexpr int kMaxSpParts = 4;
+int spatial_parts(const hc_layer_desc& d, int tile_r, int tile_c, int n_sp, int n_frames) {
+  if (d.dtype != HC_BF16 || n_sp == 0 || n_frames <= 1) return 1;
+  const int64_t wgs = (int64_t)ceil_div(d.frame_h, tile_r) * ceil_div(d.frame_w, tile_c) * n_sp;
+  const int64_t free_x = (int64_t)kNumCu * kSlotsPerCu / wgs;
+  return (int)std::max<int64_t>(1, std::min<int64_t>({free_x, kMaxSpParts, n_frames}));
+}
+
 // Items of one key range (its query tiles) are dispatched consecutively; keeping a
 // run of them on one XCD lets them share the key range through that XCD's L2.
 int xcd_group_size(int nqt) {
@@ -344,6 +356,7 @@ struct hc_head_buffers {
   std::vector<MergeEntry> merges;
   std::vector<SpatialEntry> spatials;
   int sp_tile_r = 0, sp_tile_c = 0;   // Spatial query tile
+  int sp_parts = 1;                    // Spatial workgroups per tile (frame parts)
   int n_slots = 0;
   int max_slots = -1;               // partial slots the routed workspace provides
   bool plan_only = false;            // host-only handle (hc_plan_head_buffers)
@@ -414,11 +427,24 @@ void build_plan(hc_head_buffers* b) {
   }
   b->plan_hist_len = hist_len;
   std::vector<Entry> es = make(b->next_block);
-  // slots: split heads and Spatial heads write fp32 partials
+  // Spatial tiles and frame parts
+  const bool cells = spatial_cells(d);
+  int n_sp = 0;
+  for (int h = 0; h < d.num_heads; ++h) n_sp += b->labels[h] == HC_SPATIAL;
+  if (n_sp > 0 && b->sp_tile_r == 0)
+    choose_spatial_tile(d.frame_h, d.frame_w, d.grid_h, d.grid_w, cells, n_sp, &b->sp_tile_r, &b->sp_tile_c);
+  auto parts_at = [&](int64_t next_block) {
+    const int n_all = (int)stored_frames(d, HC_SPATIAL, next_block) + (cells ? d.chunk_frames : 0);
+    return spatial_parts(d, b->sp_tile_r, b->sp_tile_c, n_sp, n_all);
+  };
+  b->sp_parts = n_sp > 0 ? parts_at(b->next_block) : 1;
+  // slots: split heads and Spatial heads write fp32 partials; a Spatial head with its
+  // frames in parts takes the current-block slot and one per part, merged afterwards
   int slot = 0;
   b->merges.clear();
   b->spatials.clear();
-  if (spatial_cells(d))
+  const int P = b->sp_parts;
+  if (cells)
     for (int h = 0; h < d.num_heads; ++h)
       if (b->labels[h] == HC_SPATIAL) {
         SpatialEntry se{};
@@ -426,6 +452,11 @@ void build_plan(hc_head_buffers* b) {
         se.head = h;
         se.cur_slot = -1;
         se.out_slot = -1;
+        if (P > 1) {
+          se.out_slot = slot;
+          b->merges.push_back(MergeEntry{h, slot, P, 0});
+          slot += P;
+        }
         b->spatials.push_back(se);
       }
   for (Entry& e : es) {
@@ -439,6 +470,12 @@ void build_plan(hc_head_buffers* b) {
       se.head = e.head;
       se.cur_slot = e.slot;
       se.out_slot = -1;
+      if (P > 1) {
+        se.cur_slot = -1;
+        se.out_slot = slot;
+        b->merges.push_back(MergeEntry{e.head, e.slot, 1 + P, 0});
+        slot += P;
+      }
       b->spatials.push_back(se);
     } else if (e.nsplit > 1) {
       e.slot = slot;
@@ -446,20 +483,19 @@ void build_plan(hc_head_buffers* b) {
       slot += e.nsplit;
     }
   }
-  if (!b->spatials.empty() && b->sp_tile_r == 0)
-    choose_spatial_tile(d.frame_h, d.frame_w, d.grid_h, d.grid_w, spatial_cells(d), (int)b->spatials.size(),
-                        &b->sp_tile_r, &b->sp_tile_c);
   b->entries = es;
   b->n_slots = slot;
   b->plan_block = b->next_block;
   // workspace sized for the full ring (the most slots any fill state needs), once
   if (b->max_slots < 0) {
-    std::vector<Entry> full = make(1 + rolling_blocks(d));
+    const int64_t full_block = 1 + rolling_blocks(d);
+    const int Pf = n_sp > 0 ? parts_at(full_block) : 1;
     int ms = 0;
-    for (const Entry& e : full) {
+    for (const Entry& e : make(full_block)) {
       const int cls = b->labels[e.head];
-      ms += (cls == HC_SPATIAL && !spatial_cells(d)) ? 1 : (e.nsplit > 1 ? e.nsplit : 0);
+      ms += cls == HC_SPATIAL ? (Pf > 1 ? 1 + Pf : 1) : (e.nsplit > 1 ? e.nsplit : 0);
     }
+    if (cells && Pf > 1) ms += n_sp * Pf;
     b->max_slots = ms;
   }
   b->max_slots = std::max(b->max_slots, slot);
@@ -687,18 +723,6 @@ hc_status hc_routed_attention(const hc_head_buffers* b, const void* q, const voi
   p.scale_log2 = d.softmax_scale * 1.4426950408889634f;
   HC_TRY(run_dense(b->entries, p, d.head_dim, bf16, s));
 
-  if (!b->merges.empty()) {
-    MergeParams m{};
-    m.part_o = part_o;
-    m.part_ml = part_ml;
-    m.out = out;
-    m.tok_stride = p.tok_stride;
-    m.lq = (int)lq;
-    m.head_dim = d.head_dim;
-    m.n_entries = (int)b->merges.size();
-    for (size_t i = 0; i < b->merges.size(); ++i) m.e[i] = b->merges[i];
-    HC_HIP(timed(K_MERGE, s, [&] { return launch_merge(m, d.head_dim, bf16, s); }));
-  }
   if (!b->spatials.empty()) {
     SpatialParams sp{};
     sp.q = q;
@@ -720,6 +744,7 @@ hc_status hc_routed_attention(const hc_head_buffers* b, const void* q, const voi
     sp.tile_c = b->sp_tile_c;
     sp.tiles_r = ceil_div(d.frame_h, sp.tile_r);
     sp.tiles_c = ceil_div(d.frame_w, sp.tile_c);
+    sp.n_parts = b->sp_parts;
     sp.scale_log2 = p.scale_log2;
     sp.cells = spatial_cells(d) ? 1 : 0;
     sp.k_cur = k_cur;
@@ -727,6 +752,18 @@ hc_status hc_routed_attention(const hc_head_buffers* b, const void* q, const voi
     sp.n_entries = (int)b->spatials.size();
     for (size_t i = 0; i < b->spatials.size(); ++i) sp.e[i] = b->spatials[i];
     HC_HIP(timed(bf16 ? K_SPATIAL : K_F32, s, [&] { return launch_spatial(sp, d.head_dim, bf16, s); }));
+  }
+  if (!b->merges.empty()) {
+    MergeParams m{};
+    m.part_o = part_o;
+    m.part_ml = part_ml;
+    m.out = out;
+    m.tok_stride = p.tok_stride;
+    m.lq = (int)lq;
+    m.head_dim = d.head_dim;
+    m.n_entries = (int)b->merges.size();
+    for (size_t i = 0; i < b->merges.size(); ++i) m.e[i] = b->merges[i];
+    HC_HIP(timed(K_MERGE, s, [&] { return launch_merge(m, d.head_dim, bf16, s); }));
   }
   return ok();
 }
@@ -897,6 +934,7 @@ hc_status hc_classify_heads(const hc_layer_desc* desc, const hc_classify_params*
   choose_spatial_tile(d.frame_h, d.frame_w, sp.grid_h, sp.grid_w, false, H, &sp.tile_r, &sp.tile_c);
   sp.tiles_r = ceil_div(d.frame_h, sp.tile_r);
   sp.tiles_c = ceil_div(d.frame_w, sp.tile_c);
+  sp.n_parts = 1;
   sp.scale_log2 = p.scale_log2;
   for (int h0 = 0; h0 < H; h0 += kMaxEntries) {
     const int n = std::min(H - h0, kMaxEntries);

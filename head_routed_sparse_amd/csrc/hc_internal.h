@@ -91,7 +91,7 @@ struct SpatialEntry {
   int64_t hist_off;   // element offset of history row 0
   int32_t head;
   int32_t cur_slot;   // partial slot of the current-block part; -1 in partial mode
-  int32_t out_slot;   // partial slot to write (partial mode), -1 in final mode
+  int32_t out_slot;   // first partial slot to write (partial mode), -1 in final mode
   int32_t pad;
 };
 
@@ -110,6 +110,8 @@ struct SpatialParams {
   int32_t grid_h, grid_w;
   int32_t tile_r, tile_c;    // query tile: rows x cols of positions (tile_r * tile_c <= kSpTileMax)
   int32_t tiles_r, tiles_c;  // position tiles per frame
+  int32_t n_parts;           // workgroups per tile, each over its share of the frames; with
+                             // more than one, part i writes the partial of slot out_slot + i
   int32_t n_entries;
   float scale_log2;
   int32_t cells;           // 1: own non-overlapping cell in every window frame (current

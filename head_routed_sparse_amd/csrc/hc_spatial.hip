@@ -29,11 +29,13 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
   __shared__ __attribute__((aligned(1024))) char ring[NS * R::kStageBytes];
   lds_char* const lds = (lds_char*)ring;
 
-  // the tiles of one XCD are neighbours, so the L2 keeps the window rows they share
+  // the tiles of one XCD are neighbours (same head, same frames), so the L2 keeps the
+  // window rows they share
   const int n_tiles = p.tiles_r * p.tiles_c;
-  const int lid = xcd_block(blockIdx.x, n_tiles * p.n_entries);
-  const SpatialEntry e = p.e[lid / n_tiles];
+  const int lid = xcd_block(blockIdx.x, n_tiles * p.n_parts * p.n_entries);
   const int tile = lid % n_tiles;
+  const int part = (lid / n_tiles) % p.n_parts;
+  const SpatialEntry e = p.e[lid / (n_tiles * p.n_parts)];
   const int tr = tile / p.tiles_c, tc = tile % p.tiles_c;
   const int fh = p.frame_h, fw = p.frame_w, S = fh * fw;
   const bool cells = p.cells != 0;
@@ -50,9 +52,12 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
   const int UW = uc1 - uc0;
   const int nU = (ur1 - ur0) * UW;
   const int nchunk = (nU + kStep - 1) / kStep;
-  // frames walked: the history (and, for cells, the current block after it)
+  // frames walked: this part's share of the history (and, for cells, of the current
+  // block after it)
   const int nh = p.n_hist_frames;
-  const int n_frames = nh + (cells ? p.chunk_frames : 0);
+  const int n_all = nh + (cells ? p.chunk_frames : 0);
+  const int f0 = part * n_all / p.n_parts, f1 = (part + 1) * n_all / p.n_parts;
+  const int n_frames = f1 - f0;
   const int n = nchunk * n_frames;   // steps
 
   const int tid = threadIdx.x;
@@ -98,9 +103,10 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
 #pragma unroll
         for (int i = 0; i < R::kLoads; ++i) tok[i] = union_tok(iu * kStep + la.ld_row[i]);
       }
-      const bool cur = ifr >= nh;
+      const int fr = f0 + ifr;
+      const bool cur = fr >= nh;
       const int64_t stride = cur ? ts : hs;
-      const int64_t fbase = (int64_t)(cur ? ifr - nh : ifr) * S * stride;
+      const int64_t fbase = (int64_t)(cur ? fr - nh : fr) * S * stride;
       const char* kb = (cur ? kcb : kh) + fbase;
       const char* vb = (cur ? vcb : vh) + fbase;
 #pragma unroll
@@ -173,12 +179,12 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
     const float l_tot = sum_halves(blk[0].l);
     const float m_s = blk[0].m;
     if (q_ok) {
-      if (cells) {   // the whole key set was walked here: normalise and write
+      if (e.out_slot >= 0) {
+        const int64_t prow = (int64_t)(e.out_slot + part) * p.lq + q_row;
+        store_partial<D>(blk[0], l_tot, p.part_o + prow * D, p.part_ml + prow * 2, half);
+      } else if (cells) {   // the whole key set was walked here: normalise and write
         uint16_t* op = (uint16_t*)p.out + (int64_t)q_row * p.tok_stride + (int64_t)e.head * D;
         store_out_bf16<D>(blk[0], 1.0f / l_tot, op, half);
-      } else if (e.out_slot >= 0) {
-        const int64_t prow = (int64_t)e.out_slot * p.lq + q_row;
-        store_partial<D>(blk[0], l_tot, p.part_o + prow * D, p.part_ml + prow * 2, half);
       } else {
         // merge with the dense current-block partial by log-sum-exp (an empty history
         // leaves m_s at the finite stand-in and weight 0)
@@ -222,7 +228,7 @@ hipError_t launch_spatial_f32(const SpatialParams& p, int head_dim, hipStream_t 
 hipError_t launch_spatial(const SpatialParams& p, int head_dim, int bf16, hipStream_t s) {
   if (p.n_entries == 0) return hipSuccess;
   if (!bf16) return launch_spatial_f32(p, head_dim, s);
-  const dim3 grid(p.tiles_r * p.tiles_c * p.n_entries), block(256);
+  const dim3 grid(p.tiles_r * p.tiles_c * p.n_parts * p.n_entries), block(256);
   if (head_dim == 128)
     hipLaunchKernelGGL(spatial_attn_bf16<128>, grid, block, 0, s, p);
   else
