@@ -80,6 +80,10 @@ hc_status check_desc(const hc_layer_desc* d) {
     return fail(HC_ERR_SHAPE, "softmax_scale must be positive and finite");
   const int64_t keys = (int64_t)d->window_frames * tokens_per_frame(*d);
   if (keys >= (int64_t(1) << 30)) return fail(HC_ERR_SHAPE, "window of %lld keys too large", (long long)keys);
+  // the kernels address the rows of one window tensor by 32-bit byte offsets
+  const int64_t bytes = keys * d->num_heads * d->head_dim * (int64_t)esize(*d);
+  if (bytes >= (int64_t(1) << 32) - (int64_t(1) << 16))
+    return fail(HC_ERR_SHAPE, "window K (or V) of %lld bytes: must stay under 4 GiB", (long long)bytes);
   return HC_OK;
 }
 

@@ -74,7 +74,8 @@ typedef struct {
   int32_t frame_h;        /* latent frame rows */
   int32_t frame_w;        /* latent frame columns */
   int32_t chunk_frames;   /* C: frames per AR block (the current block) */
-  int32_t window_frames;  /* F: window frames incl. sink and current block; F % C == 0, F >= C */
+  int32_t window_frames;  /* F: window frames incl. sink and current block; F % C == 0, F >= C;
+                             one window tensor, F*S*H*d elements, stays under 4 GiB */
   int32_t grid_h;         /* Spatial path window rows (>= 1; >= frame_h means whole frame) */
   int32_t grid_w;         /* Spatial path window columns */
   float softmax_scale;    /* usually 1/sqrt(d) */

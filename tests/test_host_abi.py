@@ -41,7 +41,7 @@ def desc_of(name="720p", **kw):
 @pytest.mark.parametrize("field,value,status", [
     ("head_dim", 96, 2), ("num_heads", 0, 2), ("num_heads", 65, 2), ("dtype", 7, 3),
     ("window_frames", 20, 2), ("chunk_frames", 0, 2), ("grid_h", 0, 2), ("frame_w", 0, 2),
-    ("softmax_scale", -1.0, 2)])
+    ("softmax_scale", -1.0, 2), ("frame_w", 30000, 2)])
 def test_desc_validation(field, value, status):
     d = desc_of(**{field: value})
     with pytest.raises(hc.HCError) as ei:
