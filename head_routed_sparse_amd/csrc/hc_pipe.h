@@ -336,7 +336,11 @@ __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D
       if (i + kAhead < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     if (j + NS - 1 < n) issue(j + NS - 1, (stage + NS - 1) % NS);
+    // raised wave priority over the PV product: the SIMD's other wave, which is then
+    // most likely in its softmax, yields issue slots to these MFMAs
+    __builtin_amdgcn_s_setprio(1);
     pv(pk, stage);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   int j = 0;
