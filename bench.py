@@ -254,7 +254,7 @@ def table6_labels(name, num_heads):
 
 def table6_mix(steps, warmup):
     """Routed layer-steps with the pages' measured head mix of each resolution
-    (Table 6 of the appendix page) instead of the configs' fixed mix."""
+    (Table 6 of the appendix page) instead of the workloads' fixed 2/3/4/3 and 3/3/3/3 mixes."""
     import torch
     from head_routed_sparse_amd import headcast as hc
     from head_routed_sparse_amd import inputs as hin
@@ -412,8 +412,8 @@ def cpu_baseline(inp, rows_per_head):
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the routed step shards over heads, but this build "
-              "runs on a single MI355X only (--gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU (--gpus 1): the routed step would shard over heads, "
+              "and no multi-GPU path is implemented.", file=sys.stderr)
         sys.exit(2)
     import torch
     from head_routed_sparse_amd import headcast as hc

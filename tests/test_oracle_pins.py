@@ -346,7 +346,7 @@ def test_pages_shapes_and_constants():
 
 def test_pages_flop_model_ratio():
     """App. B: with an 8-block window, a Sink head costs 2 of a Global head's 8 block
-    units (key count ratio 1/4); a Dummy head under this build's reading costs 1/8."""
+    units (key count ratio 1/4); a Dummy head attending the current block only costs 1/8."""
     geom = small_geom(fh=3, fw=4, C=2, F=16)
     rows = np.arange(geom.lq)
     n = {c: orc.key_set_mask(c, geom, geom.hist_frames, rows).sum() for c in (S_, D_, G_)}
