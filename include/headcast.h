@@ -144,8 +144,11 @@ hc_status hc_free_head_buffers(hc_head_buffers* buffers); /* host handle only */
 /* ---------------------------------------------------------------- routed step (Sec. 4.4)
  * out = every head's attention over its own key set, for the current block's queries
  * q [C*S][H][d] with the current block's k_cur / v_cur [C*S][H][d]. `workspace`
- * (device, >= hc_routed_workspace_bytes) holds fp32 partial results of split key
- * ranges; its contents need no initialisation. Output dtype = input dtype. */
+ * (device, >= hc_routed_workspace_bytes) holds fp32 partial results (split key ranges,
+ * the Spatial heads' current-block part and history frame parts); its contents need no
+ * initialisation. The size covers every fill state of the handle's window. Output
+ * dtype = input dtype. Calls on one handle are ordered by their streams; calls that
+ * share a workspace must not overlap. */
 hc_status hc_routed_workspace_bytes(const hc_head_buffers* buffers, size_t* bytes);
 hc_status hc_routed_attention(const hc_head_buffers* buffers, const void* q, const void* k_cur,
                               const void* v_cur, void* out, void* workspace, size_t ws_bytes,
