@@ -159,6 +159,7 @@ hipError_t timed(int kind, hipStream_t s, F&& launch) {
 struct Entry {
   int64_t hist_off;
   int32_t hist_len, cur_len, head, nsplit, split_len, slot;
+  bool whole;   // never split (the current block of a Spatial head)
 };
 
 constexpr int kSlotsPerCu = 2;    // dense workgroups resident per CU
@@ -194,32 +195,35 @@ double lpt_makespan(const std::vector<Entry>& es, int nqt) {
 }
 
 // Choose one key-split length for all entries (a multiple of the key tile): the
-// candidate with the smallest estimated makespan; splitting only when it pays.
-void plan_splits(std::vector<Entry>& es, int nqt) {
+// candidate with the smallest estimated makespan; splitting only when it pays. A
+// split entry takes one partial slot per split; candidates needing more than
+// slot_budget such slots are skipped (< 0: no limit; one split per entry always fits).
+void plan_splits(std::vector<Entry>& es, int nqt, int slot_budget) {
+  auto apply = [](Entry& e, int len) {
+    const int total = e.hist_len + e.cur_len;
+    e.nsplit = e.whole ? 1 : std::max(1, ceil_div(total, len));
+    e.split_len = std::max(kKeyTile, ceil_div(ceil_div(std::max(total, 1), e.nsplit), kKeyTile) * kKeyTile);
+  };
   int max_total = 0;
   for (const Entry& e : es) max_total = std::max(max_total, e.hist_len + e.cur_len);
-  if (max_total == 0) return;
   double best = -1;
-  int best_len = max_total;
-  for (int k = 1; k <= 16; ++k) {
+  int best_len = std::max(max_total, 1);
+  for (int k = 1; k <= 16 && max_total > 0; ++k) {
     const int len = ceil_div(ceil_div(max_total, k), kKeyTile) * kKeyTile;
     std::vector<Entry> trial = es;
+    int slots = 0;
     for (Entry& e : trial) {
-      const int total = e.hist_len + e.cur_len;
-      e.nsplit = std::max(1, ceil_div(total, len));
-      e.split_len = ceil_div(ceil_div(total, e.nsplit), kKeyTile) * kKeyTile;
+      apply(e, len);
+      if (e.nsplit > 1) slots += e.nsplit;
     }
+    if (slot_budget >= 0 && slots > slot_budget && k > 1) continue;
     const double m = lpt_makespan(trial, nqt) * (1.0 + 0.01 * (k - 1));   // mild bias to fewer splits
     if (best < 0 || m < best) {
       best = m;
       best_len = len;
     }
   }
-  for (Entry& e : es) {
-    const int total = e.hist_len + e.cur_len;
-    e.nsplit = std::max(1, ceil_div(total, best_len));
-    e.split_len = std::max(kKeyTile, ceil_div(ceil_div(std::max(total, 1), e.nsplit), kKeyTile) * kKeyTile);
-  }
+  for (Entry& e : es) apply(e, best_len);
 }
 
 // Spatial query tile (tile_r x tile_c positions, 24..32 of them): the shape with the
@@ -404,7 +408,7 @@ void build_plan(hc_head_buffers* b) {
   const int64_t S = tokens_per_frame(d);
   const int lq = (int)lq_of(d);
   const int nqt = ceil_div(lq, kDenseQ);
-  auto make = [&](int64_t next_block) {
+  auto make = [&](int64_t next_block, int slot_budget) {
     std::vector<Entry> es;
     for (int h = 0; h < d.num_heads; ++h) {
       const int cls = b->labels[h];
@@ -415,9 +419,10 @@ void build_plan(hc_head_buffers* b) {
       e.hist_off = b->head_off[h] < 0 ? 0 : b->head_off[h];
       if (cls == HC_SPATIAL && spatial_cells(d)) continue;   // served whole by the cell kernel
       if (cls != HC_SPATIAL) e.hist_len = (int)(stored_frames(d, cls, next_block) * S);
+      e.whole = cls == HC_SPATIAL;
       es.push_back(e);
     }
-    plan_splits(es, nqt);
+    plan_splits(es, nqt, slot_budget);
     return es;
   };
   // the plan depends on the state only through the stored history lengths, which stop
@@ -430,7 +435,6 @@ void build_plan(hc_head_buffers* b) {
     return;
   }
   b->plan_hist_len = hist_len;
-  std::vector<Entry> es = make(b->next_block);
   // Spatial tiles and frame parts
   const bool cells = spatial_cells(d);
   int n_sp = 0;
@@ -439,15 +443,30 @@ void build_plan(hc_head_buffers* b) {
     choose_spatial_tile(d.frame_h, d.frame_w, d.grid_h, d.grid_w, cells, n_sp, &b->sp_tile_r, &b->sp_tile_c);
   auto parts_at = [&](int64_t next_block) {
     const int n_all = (int)stored_frames(d, HC_SPATIAL, next_block) + (cells ? d.chunk_frames : 0);
-    return spatial_parts(d, b->sp_tile_r, b->sp_tile_c, n_sp, n_all);
+    return n_sp > 0 ? spatial_parts(d, b->sp_tile_r, b->sp_tile_c, n_sp, n_all) : 1;
   };
-  b->sp_parts = n_sp > 0 ? parts_at(b->next_block) : 1;
+  // partial slots of the Spatial heads: the current-block part (sliding windows) and,
+  // with frames in parts, one per part
+  auto spatial_slots = [&](int parts) {
+    return cells ? (parts > 1 ? n_sp * parts : 0) : n_sp * (parts > 1 ? 1 + parts : 1);
+  };
+  // The workspace is sized once, for the full window; every other fill state (more
+  // parts never, but possibly more key splits) plans within the same slots.
+  if (b->max_slots < 0) {
+    const int64_t full_block = 1 + rolling_blocks(d);
+    int split_slots = 0;
+    for (const Entry& e : make(full_block, -1))
+      if (e.nsplit > 1) split_slots += e.nsplit;
+    b->max_slots = spatial_slots(parts_at(full_block)) + split_slots;
+  }
+  b->sp_parts = parts_at(b->next_block);
+  const int P = b->sp_parts;
+  std::vector<Entry> es = make(b->next_block, b->max_slots - spatial_slots(P));
   // slots: split heads and Spatial heads write fp32 partials; a Spatial head with its
   // frames in parts takes the current-block slot and one per part, merged afterwards
   int slot = 0;
   b->merges.clear();
   b->spatials.clear();
-  const int P = b->sp_parts;
   if (cells)
     for (int h = 0; h < d.num_heads; ++h)
       if (b->labels[h] == HC_SPATIAL) {
@@ -465,9 +484,7 @@ void build_plan(hc_head_buffers* b) {
       }
   for (Entry& e : es) {
     const int cls = b->labels[e.head];
-    if (cls == HC_SPATIAL) {
-      e.nsplit = 1;
-      e.split_len = ceil_div(e.cur_len, kKeyTile) * kKeyTile;
+    if (cls == HC_SPATIAL) {   // planned whole
       e.slot = slot++;
       SpatialEntry se{};
       se.hist_off = b->head_off[e.head] < 0 ? 0 : b->head_off[e.head];
@@ -490,19 +507,7 @@ void build_plan(hc_head_buffers* b) {
   b->entries = es;
   b->n_slots = slot;
   b->plan_block = b->next_block;
-  // workspace sized for the full ring (the most slots any fill state needs), once
-  if (b->max_slots < 0) {
-    const int64_t full_block = 1 + rolling_blocks(d);
-    const int Pf = n_sp > 0 ? parts_at(full_block) : 1;
-    int ms = 0;
-    for (const Entry& e : make(full_block)) {
-      const int cls = b->labels[e.head];
-      ms += cls == HC_SPATIAL ? (Pf > 1 ? 1 + Pf : 1) : (e.nsplit > 1 ? e.nsplit : 0);
-    }
-    if (cells && Pf > 1) ms += n_sp * Pf;
-    b->max_slots = ms;
-  }
-  b->max_slots = std::max(b->max_slots, slot);
+  b->max_slots = std::max(b->max_slots, slot);   // (never grows: the budget above holds)
 }
 
 size_t partial_bytes(int slots, int64_t lq, int head_dim) {

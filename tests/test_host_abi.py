@@ -142,6 +142,21 @@ def test_routed_plan_covers_every_key_once(name, next_block):
         assert list(ents[:, 4]) == sorted(ents[:, 4], reverse=True)
 
 
+@pytest.mark.parametrize("name", ["tiny", "480p", "720p", "1080p"])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+def test_routed_workspace_fits_every_fill_state(name, variant):
+    """The routed workspace a handle asks for covers every later fill state of its
+    window (warm-up with a growing history, then steady state)."""
+    cfg = hin.CONFIGS[name]
+    g = cfg["geom"]
+    full = g.window_frames // g.chunk_frames - 1
+    for lab in (cfg["labels"], np.full(g.num_heads, 3, np.int32), np.full(g.num_heads, 2, np.int32),
+                np.full(g.num_heads, 0, np.int32)):
+        d = hc.make_desc(g, variant)
+        sizes = {hc.hc_routed_workspace_bytes(hc.hc_plan_head_buffers(d, lab, nb)) for nb in range(full + 4)}
+        assert len(sizes) == 1, (name, variant, lab, sizes)
+
+
 def test_reduce_statistics_and_decision_match_oracle():
     rng = np.random.default_rng(0)
     lq, d = 333, 128
