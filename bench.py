@@ -409,6 +409,31 @@ def cpu_baseline(inp, rows_per_head):
                        f"{g.frame_h}x{g.frame_w} layer (fp64 numpy, {dt:.1f} s), scaled by rows")
 
 
+def cpu_context():
+    """Host model, and the oracle on the tiny workload with one BLAS thread."""
+    from oracle import headcast_oracle as orc
+    from head_routed_sparse_amd import inputs as hin
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+    except OSError:
+        pass
+    inp = hin.config_inputs("tiny")
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            orc.routed_attention(inp)
+            dt = time.perf_counter() - t0
+    except ImportError:
+        t0 = time.perf_counter()
+        orc.routed_attention(inp)
+        dt = time.perf_counter() - t0
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)),
+            "tiny_oracle_one_thread_ms": round(dt * 1e3, 2)}
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -532,6 +557,7 @@ def main():
     if not a.no_cpu:
         print("[bench] cpu oracle sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(main_res["inp"], a.cpu_rows)
+        out["cpu_context"] = cpu_context()
     print(json.dumps(out), flush=True)
 
 
