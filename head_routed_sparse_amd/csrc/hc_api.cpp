@@ -834,11 +834,14 @@ hc_status hc_reduce_statistics(const float* per_token, int64_t lq, int32_t head_
     se += per_token[t * 4 + 3];
     cp[t] = per_token[t * 4 + 2];
   }
-  std::sort(cp.begin(), cp.end());
+  // linear interpolation between the order statistics i and i + 1 (selected, not sorted)
   const double pos = percentile / 100.0 * (double)(lq - 1);
   const int64_t i = std::min<int64_t>((int64_t)std::floor(pos), lq - 1);
   const double frac = pos - (double)i;
-  const double pct = i + 1 < lq ? cp[i] + frac * (cp[i + 1] - cp[i]) : cp[i];
+  std::nth_element(cp.begin(), cp.begin() + i, cp.end());
+  const double lo = cp[i];
+  const double hi = i + 1 < lq ? *std::min_element(cp.begin() + i + 1, cp.end()) : lo;
+  const double pct = i + 1 < lq ? lo + frac * (hi - lo) : lo;
   const double mse = se / ((double)lq * head_dim);
   out[0] = s0 / lq;
   out[1] = s1 / lq;
