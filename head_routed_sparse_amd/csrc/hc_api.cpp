@@ -17,6 +17,7 @@
 #include <mutex>
 #include <queue>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "hc_internal.h"
@@ -973,12 +974,26 @@ hc_status hc_classify_heads(const hc_layer_desc* desc, const hc_classify_params*
   std::vector<float> host((size_t)H * lq * 4);
   HC_HIP(hipMemcpyAsync(host.data(), stats, host.size() * sizeof(float), hipMemcpyDeviceToHost, s));
   HC_HIP(hipStreamSynchronize(s));
+  // per-head reductions (independent; inputs validated above, so they cannot fail) on
+  // a few host threads
+  std::vector<double> red((size_t)H * 6);
+  auto reduce = [&](int h) {
+    hc_reduce_statistics(host.data() + (size_t)h * lq * 4, lq, D, params->gamma, params->percentile,
+                         red.data() + (size_t)h * 6);
+  };
+  const int n_thr = std::max(1, std::min<int>({H, 8, (int)std::thread::hardware_concurrency()}));
+  std::vector<std::thread> pool;
+  for (int t = 1; t < n_thr; ++t)
+    pool.emplace_back([&, t] {
+      for (int h = t; h < H; h += n_thr) reduce(h);
+    });
+  for (int h = 0; h < H; h += n_thr) reduce(h);
+  for (std::thread& th : pool) th.join();
   for (int h = 0; h < H; ++h) {
-    double out6[6];
-    HC_TRY(hc_reduce_statistics(host.data() + (size_t)h * lq * 4, lq, D, params->gamma, params->percentile, out6));
-    labels_out[h] = hc_decide(out6[0], out6[1], out6[2], out6[5], params);
+    const double* o = red.data() + (size_t)h * 6;
+    labels_out[h] = hc_decide(o[0], o[1], o[2], o[5], params);
     if (stats_out)
-      for (int i = 0; i < 6; ++i) stats_out[h * 6 + i] = out6[i];
+      for (int i = 0; i < 6; ++i) stats_out[h * 6 + i] = o[i];
   }
   return ok();
 }
