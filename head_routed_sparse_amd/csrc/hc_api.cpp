@@ -1080,6 +1080,16 @@ hc_status hc_debug_routed_plan(const hc_head_buffers* b, int32_t* entries, int32
   return ok();
 }
 
+hc_status hc_debug_spatial_plan(const hc_head_buffers* b, int32_t* plan) {
+  if (!b || !plan) return fail(HC_ERR_NULL, "NULL argument");
+  const bool any = !b->spatials.empty();
+  plan[0] = any ? b->sp_tile_r : 0;
+  plan[1] = any ? b->sp_tile_c : 0;
+  plan[2] = any ? b->sp_parts : 0;
+  plan[3] = b->n_slots;
+  return ok();
+}
+
 hc_status hc_timing_enable(int32_t enable) {
   std::lock_guard<std::mutex> lk(g_time_mutex);
   g_timing = enable != 0;

@@ -73,6 +73,7 @@ _SIGS = {
                                             ctypes.POINTER(_I64)]),
     "hc_debug_gather_origins": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _I32, _I32, _P, _P]),
     "hc_debug_routed_plan": (ctypes.c_int, [_P, _P, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
+    "hc_debug_spatial_plan": (ctypes.c_int, [_P, _P]),
     "hc_timing_enable": (ctypes.c_int, [_I32]),
     "hc_timing_read": (ctypes.c_int, [_P, _P]),
 }
@@ -270,6 +271,13 @@ def hc_debug_routed_plan(buffers: HeadBuffers):
     _check(lib().hc_debug_routed_plan(buffers.handle, e.ctypes.data_as(_P), n.value, ctypes.byref(n),
                                       ctypes.byref(items)))
     return e, items.value
+
+
+def hc_debug_spatial_plan(buffers: HeadBuffers):
+    """(tile rows, tile columns, frame parts, partial slots) of the routed call."""
+    p = np.zeros(4, np.int32)
+    _check(lib().hc_debug_spatial_plan(buffers.handle, p.ctypes.data_as(_P)))
+    return tuple(int(x) for x in p)
 
 
 def hc_timing_enable(on: bool = True):

@@ -186,7 +186,10 @@ int32_t hc_decide(double cos_sink, double cos_dummy, double cos_spatial, double 
  * hc_debug_gather_origins: device int32 [S][2] = Spatial window origin (row, col) of
  * every position, computed by the device code the Spatial kernel uses.
  * hc_debug_routed_plan: the dense work entries of a routed call, host
- * [n][8] = {head, hist_rows, cur_rows, nsplit, split_len, slot, item_begin, 0}. */
+ * [n][8] = {head, hist_rows, cur_rows, nsplit, split_len, slot, item_begin, 0}.
+ * hc_debug_spatial_plan: the Spatial launch of a routed call, host [4] = {tile rows,
+ * tile columns, frame parts, partial slots of the whole call}; zeros without Spatial
+ * heads. Pure host. */
 hc_status hc_debug_slot_table(const hc_head_buffers* buffers, int32_t* frames);
 hc_status hc_debug_head_region(const hc_head_buffers* buffers, int32_t head, int64_t* k_offset,
                                int64_t* v_offset, int64_t* rows);
@@ -194,6 +197,7 @@ hc_status hc_debug_gather_origins(const hc_layer_desc* desc, int32_t grid_h, int
                                   void* r0c0, void* stream);
 hc_status hc_debug_routed_plan(const hc_head_buffers* buffers, int32_t* entries, int32_t max_entries,
                                int32_t* n_entries, int32_t* n_items);
+hc_status hc_debug_spatial_plan(const hc_head_buffers* buffers, int32_t* plan);
 
 /* ---------------------------------------------------------------- timing
  * When enabled, every kernel the library launches is bracketed by HIP events on its

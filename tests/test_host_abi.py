@@ -1,6 +1,7 @@
 """Host-side checks of the C ABI that need no GPU: the library loads and exports every
 declared symbol, argument validation, buffer sizes, the ring slot table, the routed
 work plan, and the classifier's host reductions against the oracle."""
+import dataclasses
 import os
 import re
 
@@ -155,6 +156,36 @@ def test_routed_workspace_fits_every_fill_state(name, variant):
         d = hc.make_desc(g, variant)
         sizes = {hc.hc_routed_workspace_bytes(hc.hc_plan_head_buffers(d, lab, nb)) for nb in range(full + 4)}
         assert len(sizes) == 1, (name, variant, lab, sizes)
+
+
+@pytest.mark.parametrize("name,variant,want", [("720p", 0, (5, 6, 1)), ("480p", 0, (5, 6, 3)),
+                                               ("1080p", 0, (4, 8, 1)), ("720p", 2, (5, 5, 1)),
+                                               ("480p", 2, (5, 5, 2))])
+def test_spatial_plan(name, variant, want):
+    """Spatial tile and frame parts at the bench sizes: 24..32 positions inside the frame,
+    parts only while the tiles leave workgroup slots free, at most one per frame, and
+    the partial slots (current block + one per part per Spatial head, plus the key
+    splits) within the workspace."""
+    cfg = hin.CONFIGS[name]
+    g = cfg["geom"]
+    if variant & 2:   # the pages' 10 x 10 cells
+        g = dataclasses.replace(g, grid_h=10, grid_w=10)
+    lab = cfg["labels"]
+    n_sp = int((lab == 2).sum())
+    pb = hc.hc_plan_head_buffers(hc.make_desc(g, variant), lab, g.window_frames // g.chunk_frames - 1)
+    tr, tc, parts, slots = hc.hc_debug_spatial_plan(pb)
+    assert (tr, tc, parts) == want
+    assert 24 <= tr * tc <= 32 and tr <= g.frame_h and tc <= g.frame_w
+    tiles = -(-g.frame_h // tr) * -(-g.frame_w // tc) * n_sp
+    assert parts == max(1, min(512 // tiles, 4, g.hist_frames + (g.chunk_frames if variant & 2 else 0)))
+    ents, _ = hc.hc_debug_routed_plan(pb)
+    split_slots = int(sum(e[3] for e in ents if e[3] > 1))
+    sp_slots = (n_sp * parts if parts > 1 else 0) if variant & 2 else n_sp * (1 + parts if parts > 1 else 1)
+    assert slots == split_slots + sp_slots
+    assert hc.hc_routed_workspace_bytes(pb) >= slots * g.lq * (g.head_dim + 2) * 4
+    # no Spatial heads: no Spatial launch
+    assert hc.hc_debug_spatial_plan(hc.hc_plan_head_buffers(hc.make_desc(g), np.full(g.num_heads, 3, np.int32),
+                                                            1))[:3] == (0, 0, 0)
 
 
 def test_reduce_statistics_and_decision_match_oracle():
