@@ -6,13 +6,16 @@
 // A workgroup (4 waves) takes a tile of up to 32 positions (tile_r x tile_c, chosen by
 // the host) of one Spatial head, one wave per chunk frame (the chunk frames at one
 // position share the key set exactly; with three chunk frames the fourth wave only
-// loads). It walks the union of the tile's windows in 32-key steps, chunk-outer and frame-inner, on the dense kernel's pipeline
-// (hc_pipe.h): every step's rows are gathered whole (256 B) by 16-byte direct loads
-// into the LDS ring, and keys outside a query's own window are masked. The union
-// position of every row a lane loads, and every lane's mask bits, depend only on the
-// chunk, so they are computed once per chunk. In final mode the result is merged with
-// the dense current-block partial by its log-sum-exp and written as bf16; in partial
-// mode (classifier) it is stored as fp32; with cells the whole key set is walked here.
+// loads). It walks the union of the tile's windows in 32-key steps, chunk-outer and
+// frame-inner, on the dense kernel's pipeline (hc_pipe.h): every step's rows are
+// gathered whole (256 B) by 16-byte direct loads into the LDS ring. The union position
+// of every row a lane loads, and every lane's window bits, depend only on the chunk, so
+// they are computed once per chunk; the window mask is folded into the exponent's
+// addend (-inf outside the window). With frame parts, each of n_parts workgroups walks
+// its share of the frames and stores an fp32 partial that the merge kernel joins. In
+// final mode the result is merged with the dense current-block partial by its
+// log-sum-exp and written as bf16; in partial mode (classifier, frame parts) it is
+// stored as fp32; with cells the whole key set is walked here.
 #include "hc_pipe.h"
 
 namespace hc {
