@@ -67,6 +67,26 @@ def spatial_work(geom, labels, n_hist):
     return flops, byts
 
 
+def spatial_mfma_flops(geom, n_sp, n_hist, tile_r, tile_c):
+    """Flops the Spatial kernel issues on the matrix cores: each 32-row query block
+    (one chunk frame of a tile) runs over the union of its tile's windows in whole
+    32-key steps, in every history frame."""
+    fh, fw, gh, gw = geom.frame_h, geom.frame_w, geom.grid_h, geom.grid_w
+
+    def org(p, g, ext):
+        return min(max(p - g // 2, 0), max(ext - g, 0))
+
+    steps = 0
+    for r0 in range(0, fh, tile_r):
+        r1 = min(r0 + tile_r, fh) - 1
+        ur = org(r1, gh, fh) + min(gh, fh) - org(r0, gh, fh)
+        for c0 in range(0, fw, tile_c):
+            c1 = min(c0 + tile_c, fw) - 1
+            uc = org(c1, gw, fw) + min(gw, fw) - org(c0, gw, fw)
+            steps += -(-ur * uc // 32)
+    return 4.0 * 32 * 32 * geom.head_dim * steps * n_hist * geom.chunk_frames * n_sp
+
+
 KERNEL_SOURCES = ["hc_dense.hip", "hc_pipe.h", "hc_mfma.h", "hc_internal.h"]
 COUNTERS = os.path.join(ROOT, "profiles", "dense_attn_bf16_720p_counters.json")
 
@@ -144,7 +164,7 @@ def measure(name, steps, warmup, with_events, only_routed=False, labels_override
             hc.hc_timing_enable(False)
             kern = {k: (v[0] / max(v[1], 1), v[1]) for k, v in hc.hc_timing_read().items() if v[1]}
         res[tag] = dict(ms=ms, kernels=kern, labels=labels, call_median=float(np.median(call_ms)),
-                        call_min=float(call_ms.min()))
+                        call_min=float(call_ms.min()), spatial_plan=hc.hc_debug_spatial_plan(buf))
         del buf, ws, out
     res["geom"] = g
     res["inp"] = inp
@@ -409,6 +429,21 @@ def cpu_baseline(inp, rows_per_head):
                        f"{g.frame_h}x{g.frame_w} layer (fp64 numpy, {dt:.1f} s), scaled by rows")
 
 
+def spatial_gather(g, r, n_hist, sp_flops, sp_bytes):
+    """The Spatial kernel against HBM (unique bytes) and against the matrix cores (the
+    flops it issues, union steps included)."""
+    if "spatial" not in r["kernels"]:
+        return None
+    ms = r["kernels"]["spatial"][0]
+    tile_r, tile_c, parts, _ = r["spatial_plan"]
+    n_sp = int((np.asarray(r["labels"]) == 2).sum())
+    mf = spatial_mfma_flops(g, n_sp, n_hist, tile_r, tile_c)
+    return {"flops": sp_flops, "unique_bytes": sp_bytes, "avg_ms": round(ms, 4),
+            "hbm_frac": round(sp_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "tile": [tile_r, tile_c], "frame_parts": parts, "mfma_flops": mf,
+            "mfma_frac": round(mf / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def cpu_context():
     """Host model, and the oracle on the tiny workload with one BLAS thread."""
     from oracle import headcast_oracle as orc
@@ -504,10 +539,7 @@ def main():
                      "kernel": "dense_attn_bf16<128, 1>", "flops_per_launch": dflops},
         "full_window_roofline_frac": round(dense_flops(g, base["labels"], n_hist) /
                                            (base["kernels"]["dense"][0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "spatial_gather": {"flops": sp_flops, "unique_bytes": sp_bytes,
-                           "avg_ms": round(r["kernels"].get("spatial", (0, 0))[0], 4),
-                           "hbm_frac": round(sp_bytes / (r["kernels"]["spatial"][0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-                           if "spatial" in r["kernels"] else None},
+        "spatial_gather": spatial_gather(g, r, n_hist, sp_flops, sp_bytes),
         "copies": {"build_bytes": main_res["build_bytes"], "build_kernel_ms": round(main_res["build_kernel_ms"], 4),
                    "build_hbm_frac": round(main_res["build_bytes"] / (main_res["build_kernel_ms"] * 1e-3) / 1e9 /
                                            PEAK_HBM_GBS, 4),
