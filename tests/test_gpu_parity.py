@@ -80,6 +80,26 @@ def test_spatial_grids(grid):
         assert_close(got, got_g, 2e-3, 2e-4, what="spatial==global")
 
 
+@pytest.mark.parametrize("frame", [(3, 40), (40, 3), (2, 2), (1, 50), (7, 7), (5, 6)])
+@pytest.mark.parametrize("variant", [0, 2])
+def test_spatial_tiles_on_odd_frames(frame, variant):
+    """Frames narrower or shorter than any 24..32-position tile, or smaller than 24
+    positions (the 4 x 8 fallback tile), with several frame parts and, for the cell
+    variant, cells cut at the frame edge."""
+    fh, fw = frame
+    g = hin.Geometry(4, 128, fh, fw, 3, 12, 3, 4, "bf16")
+    inp = hin.generate(g, (P_, G_, P_, S_), seed=fh * 100 + fw + variant)
+    t = to_device(inp)
+    buf = hc.hc_build_head_buffers(hc.make_desc(g, variant), inp.labels, t["k_hist"], t["v_hist"],
+                                   inp.n_hist_frames)
+    tile_r, tile_c, parts, _ = hc.hc_debug_spatial_plan(buf)
+    assert tile_r * tile_c <= 32 and parts >= 1
+    got = host(hc.hc_routed_attention(buf, t["q"], t["k_cur"], t["v_cur"]))
+    want = orc.routed_attention(inp, variant=variant)
+    print(frame, variant, (tile_r, tile_c, parts),
+          assert_close(got, want, *TOL["bf16"], what=f"{frame} v{variant} tile {tile_r}x{tile_c} parts {parts}"))
+
+
 def test_one_block_window_all_paths_agree():
     g = hin.Geometry(4, 128, 7, 9, 2, 2, 3, 3, "bf16")
     inp = hin.generate(g, (S_, D_, P_, G_), seed=5)
