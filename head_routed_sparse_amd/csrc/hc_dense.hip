@@ -131,7 +131,7 @@ void dense_attn_bf16(const DenseParams p) {
     if (last) mask_last(sc);
     softmax_step(blk, sc, c, pk);
   };
-  run_steps<D, QB, W, NS>(n, lds, la, q, blk, true, issue, [] {}, soft);
+  run_steps<D, QB, W, NS, false>(n, lds, la, q, blk, true, issue, [] {}, soft);
 
   // outputs
 #pragma unroll

@@ -251,7 +251,10 @@ struct LaneAddr {
 // instructions, and the last step lands on stage 0 with its scores in the first buffer.
 //   active:          false for a wave with no queries of its own: it still issues its
 //                    share of the loads and meets every barrier, but skips the math.
-template <int D, int QB, int W, int NS, class Issue, class Prep, class Soft>
+//   kEarlyV:         read the step's V^T fragments right after the barrier (their stage
+//                    stays put for the whole step) instead of just before the PV product:
+//                    32 more live registers, less exposed LDS latency per step.
+template <int D, int QB, int W, int NS, bool kEarlyV, class Issue, class Prep, class Soft>
 __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D, QB, W>& la,
                                           const u32x4 (&q)[QB][D / 16], Block<D> (&blk)[QB], bool active,
                                           Issue&& issue, Prep&& prep, Soft&& soft) {
@@ -272,7 +275,8 @@ __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D
     }
   };
   // O^T += V^T P^T of a step for every block (each V^T fragment read once, used QB times)
-  auto pv = [&](const u32x4 (&pk)[QB][2], int stage) {
+  // V^T fragments of a step
+  auto read_v = [&](u32x4 (&vf)[2][DB], int stage) {
     const lds_char* base = lds + stage * R::kStageBytes;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
@@ -283,9 +287,28 @@ __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4*)(base + la.v[db][1] + s2 * 16 * R::kRowBytes));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        const u32x4 vf = {l2[0], l2[1], h2[0], h2[1]};
+        vf[s2][db] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+      }
+  };
+  // O^T += V^T P^T of a step for every block (each V^T fragment used QB times), from
+  // fragments read before, or (stage >= 0) read here, each just before its products
+  auto pv = [&](const u32x4 (&pk)[QB][2], const u32x4 (&vf)[2][DB], int stage) {
+    const lds_char* base = lds + (stage < 0 ? 0 : stage) * R::kStageBytes;
 #pragma unroll
-        for (int b = 0; b < QB; ++b) blk[b].o[db] = mfma32(vf, pk[b][s2], blk[b].o[db]);
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        u32x4 v = vf[s2][db];
+        if (stage >= 0) {
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(base + la.v[db][0] + s2 * 16 * R::kRowBytes));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(base + la.v[db][1] + s2 * 16 * R::kRowBytes));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+          v = u32x4{l2[0], l2[1], h2[0], h2[1]};
+        }
+#pragma unroll
+        for (int b = 0; b < QB; ++b) blk[b].o[db] = mfma32(v, pk[b][s2], blk[b].o[db]);
       }
   };
 
@@ -319,6 +342,8 @@ __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D
     }
     prep();
     scores(sn, (stage + 1) % NS);
+    u32x4 vf[2][DB] = {};
+    if (kEarlyV) read_v(vf, stage);
     u32x4 pk[QB][2];
     soft(sc, pk, false);
     // issue in order: alternate each score MFMA with the exponentials that fit under
@@ -339,7 +364,7 @@ __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D
     // raised wave priority over the PV product: the SIMD's other wave, which is then
     // most likely in its softmax, yields issue slots to these MFMAs
     __builtin_amdgcn_s_setprio(1);
-    pv(pk, stage);
+    pv(pk, vf, kEarlyV ? -1 : stage);
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -362,9 +387,11 @@ __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D
   // last step (stage 0, scores in s0)
   if (!active) return;
   prep();
+  u32x4 vf[2][DB] = {};
+  if (kEarlyV) read_v(vf, 0);
   u32x4 pk[QB][2];
   soft(s0, pk, true);
-  pv(pk, 0);
+  pv(pk, vf, kEarlyV ? -1 : 0);
 }
 
 }  // namespace hc

@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
       blk[0].l += ls;
     };
 
-    if (n > 0) run_steps<D, 1, W, NS>(n, lds, la, q, blk, active, issue, prep, soft);
+    if (n > 0) run_steps<D, 1, W, NS, true>(n, lds, la, q, blk, active, issue, prep, soft);
     __syncthreads();   // the ring is reused by the next group of chunk frames
 
     const float l_tot = sum_halves(blk[0].l);
