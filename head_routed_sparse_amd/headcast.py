@@ -3,6 +3,17 @@
 Argument marshalling only: every step runs in the library's HIP kernels. Device
 memory is torch tensors (their data_ptr), streams are torch's current HIP stream.
 The functions keep the C names. Loading fails loudly when the library is missing.
+
+One layer of an autoregressive rollout (tensors [tokens][H][d] bf16 on the GPU):
+
+    desc = make_desc(geometry)                       # or LayerDesc(...) by hand
+    labels, stats = hc_classify_heads(desc, hc_default_classify_params(), q, k_hist,
+                                      v_hist, n_hist_frames, k_cur, v_cur)  # once
+    buf = hc_build_head_buffers(desc, labels, k_hist, v_hist, n_hist_frames)
+    ws = routed_workspace(buf)                       # serves every later fill state
+    for each denoising step of the block:
+        out = hc_routed_attention(buf, q, k_cur, v_cur, workspace=ws)
+    hc_append_chunk(buf, k_cur, v_cur)               # the finished block enters the ring
 """
 from __future__ import annotations
 
