@@ -124,6 +124,34 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _elem(desc):
+    """torch dtype of a layer's tensors."""
+    import torch
+    return torch.bfloat16 if desc.dtype == HC_BF16 else torch.float32
+
+
+def _dev(t, name, dtype=None, numel=0):
+    """Device pointer of a tensor the kernels read or write: a contiguous GPU tensor of
+    the layer's dtype with at least `numel` elements (the C ABI sees only the pointer,
+    so these are checked here, before any call)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise HCError(7, f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise HCError(2, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise HCError(3, f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.numel() < numel:
+        raise HCError(2, f"{name} has {t.numel()} elements, needs {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _block_numel(desc):
+    """Elements of one block's [C*S][H][d] tensor."""
+    return desc.chunk_frames * desc.frame_h * desc.frame_w * desc.num_heads * desc.head_dim
+
+
 def make_desc(geom, variant: int = 0) -> LayerDesc:
     """LayerDesc from an object with the Geometry fields (see inputs.Geometry)."""
     return LayerDesc(geom.num_heads, geom.head_dim, geom.frame_h, geom.frame_w,
@@ -169,12 +197,16 @@ def hc_build_head_buffers(desc: LayerDesc, labels, k_hist, v_hist, n_hist_frames
     import torch
     lab = _labels_arr(labels)
     nbytes = hc_head_buffers_bytes(desc, lab)
+    hist = int(n_hist_frames) * desc.frame_h * desc.frame_w * desc.num_heads * desc.head_dim
+    kp = _dev(k_hist, "k_hist", _elem(desc), hist)
+    vp = _dev(v_hist, "v_hist", _elem(desc), hist)
     if memory is None:
         memory = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    mp = _dev(memory, "memory", torch.uint8)
     h = _P()
-    _check(lib().hc_build_head_buffers(ctypes.byref(desc), lab.ctypes.data_as(_P), _ptr(k_hist),
-                                       _ptr(v_hist), int(n_hist_frames), _ptr(memory),
-                                       memory.numel(), ctypes.byref(h), _stream(stream)))
+    _check(lib().hc_build_head_buffers(ctypes.byref(desc), lab.ctypes.data_as(_P), kp, vp,
+                                       int(n_hist_frames), mp, memory.numel(), ctypes.byref(h),
+                                       _stream(stream)))
     return HeadBuffers(h, memory, desc)
 
 
@@ -187,7 +219,9 @@ def hc_plan_head_buffers(desc: LayerDesc, labels, next_block: int) -> HeadBuffer
 
 
 def hc_append_chunk(buffers: HeadBuffers, k_chunk, v_chunk, stream=None):
-    _check(lib().hc_append_chunk(buffers.handle, _ptr(k_chunk), _ptr(v_chunk), _stream(stream)))
+    d, n = buffers.desc, _block_numel(buffers.desc)
+    _check(lib().hc_append_chunk(buffers.handle, _dev(k_chunk, "k_chunk", _elem(d), n),
+                                 _dev(v_chunk, "v_chunk", _elem(d), n), _stream(stream)))
 
 
 def hc_buffers_state(buffers: HeadBuffers) -> int:
@@ -209,12 +243,17 @@ def routed_workspace(buffers: HeadBuffers):
 
 def hc_routed_attention(buffers: HeadBuffers, q, k_cur, v_cur, out=None, workspace=None, stream=None):
     import torch
+    d, n = buffers.desc, _block_numel(buffers.desc)
+    qp = _dev(q, "q", _elem(d), n)
+    kp = _dev(k_cur, "k_cur", _elem(d), n)
+    vp = _dev(v_cur, "v_cur", _elem(d), n)
     if out is None:
         out = torch.empty_like(q)
+    op = _dev(out, "out", _elem(d), n)
     if workspace is None:
         workspace = routed_workspace(buffers)
-    _check(lib().hc_routed_attention(buffers.handle, _ptr(q), _ptr(k_cur), _ptr(v_cur), _ptr(out),
-                                     _ptr(workspace), workspace.numel(), _stream(stream)))
+    wp = _dev(workspace, "workspace", torch.uint8)
+    _check(lib().hc_routed_attention(buffers.handle, qp, kp, vp, op, wp, workspace.numel(), _stream(stream)))
     return out
 
 
@@ -229,16 +268,21 @@ def hc_classify_heads(desc: LayerDesc, params: ClassifyParams, q, k_hist, v_hist
                       k_cur, v_cur, workspace=None, stream=None):
     """Returns (labels int32 [H], stats float64 [H][6])."""
     import torch
+    n = _block_numel(desc)
+    hist = int(n_hist_frames) * desc.frame_h * desc.frame_w * desc.num_heads * desc.head_dim
+    ptrs = [_dev(q, "q", _elem(desc), n), _dev(k_hist, "k_hist", _elem(desc), hist),
+            _dev(v_hist, "v_hist", _elem(desc), hist), _dev(k_cur, "k_cur", _elem(desc), n),
+            _dev(v_cur, "v_cur", _elem(desc), n)]
     if workspace is None:
         workspace = torch.empty(hc_classify_workspace_bytes(desc, params, n_hist_frames),
                                 dtype=torch.uint8, device="cuda")
+    wp = _dev(workspace, "workspace", torch.uint8)
     H = desc.num_heads
     labels = np.zeros(H, np.int32)
     stats = np.zeros((H, 6), np.float64)
-    _check(lib().hc_classify_heads(ctypes.byref(desc), ctypes.byref(params), _ptr(q), _ptr(k_hist),
-                                   _ptr(v_hist), int(n_hist_frames), _ptr(k_cur), _ptr(v_cur),
-                                   _ptr(workspace), workspace.numel(), labels.ctypes.data_as(_P),
-                                   stats.ctypes.data_as(_P), _stream(stream)))
+    _check(lib().hc_classify_heads(ctypes.byref(desc), ctypes.byref(params), ptrs[0], ptrs[1], ptrs[2],
+                                   int(n_hist_frames), ptrs[3], ptrs[4], wp, workspace.numel(),
+                                   labels.ctypes.data_as(_P), stats.ctypes.data_as(_P), _stream(stream)))
     return labels, stats
 
 

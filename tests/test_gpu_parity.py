@@ -100,6 +100,23 @@ def test_spatial_tiles_on_odd_frames(frame, variant):
           assert_close(got, want, *TOL["bf16"], what=f"{frame} v{variant} tile {tile_r}x{tile_c} parts {parts}"))
 
 
+def test_binding_rejects_bad_tensors():
+    """Wrong dtype, too few elements or a strided view: refused before the library runs."""
+    g = hin.Geometry(4, 64, 8, 8, 1, 5, 3, 3, "bf16")
+    inp = hin.generate(g, (S_, D_, P_, G_), seed=9)
+    t = to_device(inp)
+    buf = hc.hc_build_head_buffers(hc.make_desc(g), inp.labels, t["k_hist"], t["v_hist"], inp.n_hist_frames)
+    q = t["q"]
+    for bad, status in ((q.float(), 3), (q[: q.shape[0] // 2], 2), (q.transpose(1, 2), 2)):
+        with pytest.raises(hc.HCError) as ei:
+            hc.hc_routed_attention(buf, bad, t["k_cur"], t["v_cur"])
+        assert ei.value.status == status
+    with pytest.raises(hc.HCError) as ei:
+        hc.hc_append_chunk(buf, t["k_cur"][:1], t["v_cur"])
+    assert ei.value.status == 2
+    torch.cuda.synchronize()
+
+
 def test_one_block_window_all_paths_agree():
     g = hin.Geometry(4, 128, 7, 9, 2, 2, 3, 3, "bf16")
     inp = hin.generate(g, (S_, D_, P_, G_), seed=5)

@@ -188,6 +188,24 @@ def test_spatial_plan(name, variant, want):
                                                             1))[:3] == (0, 0, 0)
 
 
+def test_binding_rejects_host_tensors():
+    """The binding passes raw device pointers, so it refuses host tensors before any call."""
+    import torch
+    g = hin.CONFIGS["tiny"]["geom"]
+    d = hc.make_desc(g)
+    lab = hin.CONFIGS["tiny"]["labels"]
+    x = torch.zeros((g.lq, g.num_heads, g.head_dim), dtype=torch.float32)
+    with pytest.raises(hc.HCError) as ei:
+        hc.hc_build_head_buffers(d, lab, x, x, g.chunk_frames)
+    assert ei.value.status == 7
+    pb = hc.hc_plan_head_buffers(d, lab, 1)
+    for call in (lambda: hc.hc_routed_attention(pb, x, x, x), lambda: hc.hc_append_chunk(pb, x, x),
+                 lambda: hc.hc_classify_heads(d, hc.hc_default_classify_params(), x, x, x, g.chunk_frames, x, x)):
+        with pytest.raises(hc.HCError) as ei:
+            call()
+        assert ei.value.status == 7
+
+
 def test_reduce_statistics_and_decision_match_oracle():
     rng = np.random.default_rng(0)
     lq, d = 333, 128
