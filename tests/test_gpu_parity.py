@@ -332,6 +332,21 @@ def test_classify_unplanted_statistics_match_oracle():
         assert np.allclose(stats[h], ref, atol=3e-3), (h, stats[h], ref)
 
 
+@pytest.mark.parametrize("proxy", [(5, 5), (2, 7), (1, 1)])
+def test_classify_proxy_grid_statistics_match_oracle(proxy):
+    """A Spatial proxy window other than the routing grid (the pages' radius-2, 5 x 5
+    proxy for the deployed cells; non-square; a single key per frame)."""
+    g = hin.Geometry(4, 128, 9, 14, 2, 8, 3, 3, "bf16")
+    inp = hin.generate(g, [G_, P_, G_, P_], seed=10 + proxy[0], planted=True)
+    got, stats = classify_gpu(inp, gamma=0.5, proxy_grid_h=proxy[0], proxy_grid_w=proxy[1])
+    want, ost = orc.classify_heads(inp, dict(gamma=0.5, proxy_grid=proxy))
+    for h in range(4):
+        o = ost[h]
+        ref = [o["cos_sink"], o["cos_dummy"], o["cos_spatial"], o["p5"], o["mse"], o["score"]]
+        assert np.allclose(stats[h], ref, atol=3e-3), (proxy, h, stats[h], ref)
+    assert list(got) == list(want)
+
+
 def test_classify_sink_proxy_variant():
     g = hin.Geometry(2, 128, 12, 20, 3, 21, 8, 8, "bf16")
     inp = hin.generate(g, [D_, G_], seed=6, planted=True)
