@@ -163,15 +163,19 @@ struct Entry {
   bool whole;   // never split (the current block of a Spatial head)
 };
 
-constexpr int kSlotsPerCu = 2;    // dense workgroups resident per CU
+constexpr int kSlotsPerCu = 2;    // Spatial (and d = 128 dense) workgroups resident per CU
 constexpr int kNumCu = 256;
+
+// Dense workgroups resident per CU: d = 128 fills half the LDS and registers with two,
+// d = 64 (a 32 KB ring, 119 registers) takes four.
+int dense_slots(int head_dim) { return kNumCu * (head_dim == 64 ? 4 : kSlotsPerCu); }
 constexpr double kItemOverheadTiles = 3.0;
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 // Makespan estimate (in key tiles) of LPT list scheduling of the entries' items on
-// kNumCu * kSlotsPerCu slots; items run in order of decreasing length.
-double lpt_makespan(const std::vector<Entry>& es, int nqt) {
+// n_slots workgroup slots; items run in order of decreasing length.
+double lpt_makespan(const std::vector<Entry>& es, int nqt, int n_slots) {
   std::vector<std::pair<double, int64_t>> items;   // (cost, count)
   for (const Entry& e : es) {
     const int total = e.hist_len + e.cur_len;
@@ -183,7 +187,7 @@ double lpt_makespan(const std::vector<Entry>& es, int nqt) {
   }
   std::sort(items.begin(), items.end(), [](auto& a, auto& b) { return a.first > b.first; });
   std::priority_queue<double, std::vector<double>, std::greater<double>> slots;
-  for (int i = 0; i < kNumCu * kSlotsPerCu; ++i) slots.push(0.0);
+  for (int i = 0; i < n_slots; ++i) slots.push(0.0);
   double makespan = 0.0;
   for (auto& it : items)
     for (int64_t c = 0; c < it.second; ++c) {
@@ -199,7 +203,8 @@ double lpt_makespan(const std::vector<Entry>& es, int nqt) {
 // candidate with the smallest estimated makespan; splitting only when it pays. A
 // split entry takes one partial slot per split; candidates needing more than
 // slot_budget such slots are skipped (< 0: no limit; one split per entry always fits).
-void plan_splits(std::vector<Entry>& es, int nqt, int slot_budget) {
+// n_slots: dense workgroups the GPU runs at once.
+void plan_splits(std::vector<Entry>& es, int nqt, int slot_budget, int n_slots) {
   auto apply = [](Entry& e, int len) {
     const int total = e.hist_len + e.cur_len;
     e.nsplit = e.whole ? 1 : std::max(1, ceil_div(total, len));
@@ -218,7 +223,7 @@ void plan_splits(std::vector<Entry>& es, int nqt, int slot_budget) {
       if (e.nsplit > 1) slots += e.nsplit;
     }
     if (slot_budget >= 0 && slots > slot_budget && k > 1) continue;
-    const double m = lpt_makespan(trial, nqt) * (1.0 + 0.01 * (k - 1));   // mild bias to fewer splits
+    const double m = lpt_makespan(trial, nqt, n_slots) * (1.0 + 0.01 * (k - 1));   // mild bias to fewer splits
     if (best < 0 || m < best) {
       best = m;
       best_len = len;
@@ -423,7 +428,7 @@ void build_plan(hc_head_buffers* b) {
       e.whole = cls == HC_SPATIAL;
       es.push_back(e);
     }
-    plan_splits(es, nqt, slot_budget);
+    plan_splits(es, nqt, slot_budget, dense_slots(d.head_dim));
     return es;
   };
   // the plan depends on the state only through the stored history lengths, which stop

@@ -9,11 +9,12 @@
 // ordered longest first and grouped per XCD so that the query tiles sharing a key
 // range run on the same L2.
 //
-// For D=128 a workgroup is four waves of 32 queries (one per SIMD, all state in VGPRs)
-// and two workgroups share a CU, each with its own LDS ring and barrier, so that one's
-// softmax overlaps the other's MFMAs; for D=64, two waves of two 32-query blocks, where
-// each K or V fragment read from LDS feeds one MFMA per block. The step pipeline (direct
-// loads into an LDS ring, transposed V reads, reference-max softmax) is in hc_pipe.h.
+// A workgroup is four waves of 32 queries (one per SIMD, all state in VGPRs). For D=128
+// two workgroups share a CU, each with its own LDS ring and barrier, so that one's
+// softmax overlaps the other's MFMAs; for D=64 (119 registers, a 32 KB ring) four do,
+// which the softmax needs more, with half the matrix work per score. The step pipeline
+// (direct loads into an LDS ring, transposed V reads, reference-max softmax) is in
+// hc_pipe.h.
 #include "hc_pipe.h"
 
 namespace hc {
@@ -160,10 +161,10 @@ hipError_t launch_dense_f32(const DenseParams& p, int head_dim, hipStream_t s);
 hipError_t launch_dense(const DenseParams& p, int head_dim, int bf16, hipStream_t s) {
   if (p.n_items == 0) return hipSuccess;
   if (!bf16) return launch_dense_f32(p, head_dim, s);
-  // D=128: four waves of 32 queries; D=64: two waves of 64 queries
+  // four waves of 32 queries for both head sizes
   const dim3 grid(dense_items_grid(p.n_items, p.xcd_group));
   if (head_dim == 64)
-    hipLaunchKernelGGL((dense_attn_bf16<64, 2>), grid, dim3(64 * (kDenseQ / 64)), 0, s, p);
+    hipLaunchKernelGGL((dense_attn_bf16<64, 1>), grid, dim3(64 * (kDenseQ / 32)), 0, s, p);
   else
     hipLaunchKernelGGL((dense_attn_bf16<128, 1>), grid, dim3(64 * (kDenseQ / 32)), 0, s, p);
   return hipGetLastError();
