@@ -437,3 +437,46 @@ def test_variant_dummy_buffer_holds_latest_block(F, C):
             want[:C] = np.arange(b * C, b * C + C)
         assert np.array_equal(tab[1], want)
         assert np.array_equal(tab[[0, 2, 3]], orc.slot_table([S_, P_, G_], F, C, n))
+
+
+# ----------------------------------------------------------------------------- routing and proxy pins
+def test_p1_routed_mixed_labels_follow_each_heads_own_class():
+    """Routing (Sec. 4.4): on an unsorted mix of classes, head h's output is the brute
+    force attention over the key set of ITS OWN label, row by row."""
+    geom = small_geom(fh=5, fw=7, C=2, F=8, g=3, H=6)
+    labels = [G_, S_, P_, D_, D_, G_]
+    inp = small_inputs(geom, seed=31, labels=labels)
+    out = orc.routed_attention(inp)
+    for h, cls in enumerate(labels):
+        for t in range(geom.lq):
+            bf = orc.brute_force_attention(inp, h, cls, t)
+            assert np.max(np.abs(out[t, h] - bf)) < 1e-12, (h, cls, t)
+    # and a different class gives a different answer for every non-Global head here
+    for h, cls in enumerate(labels):
+        other = G_ if cls != G_ else D_
+        assert np.max(np.abs(out[:, h] - orc.path_attention(inp, h, other))) > 1e-3
+
+
+def test_p11_classify_with_proxy_grid_uses_that_grid():
+    """Classification (Sec. 4.2, Eqs. 3-5) with a Spatial proxy window other than the
+    routing grid: the statistics equal those built from brute-force outputs of the
+    reference, the three proxies and the 5 x 5 window, and differ from the routing grid's."""
+    geom = small_geom(fh=7, fw=9, C=2, F=8, g=3, d=16, H=4)
+    labels = [P_, G_, P_, D_]
+    inp = small_inputs(geom, seed=32, labels=labels, planted=True)
+    proxy = (5, 5)
+    got_labels, got = orc.classify_heads(inp, dict(gamma=0.5, proxy_grid=proxy))
+    rows = range(geom.lq)
+    for h in range(geom.num_heads):
+        ref = np.array([orc.brute_force_attention(inp, h, G_, t) for t in rows])
+        snk = np.array([orc.brute_force_attention(inp, h, S_, t, sink_proxy=True) for t in rows])
+        dum = np.array([orc.brute_force_attention(inp, h, D_, t) for t in rows])
+        spa = np.array([orc.brute_force_attention(inp, h, P_, t, grid=proxy) for t in rows])
+        spa_routing = np.array([orc.brute_force_attention(inp, h, P_, t) for t in rows])
+        want = orc.head_statistics(snk, dum, spa, ref, gamma=0.5)
+        for k in ("cos_sink", "cos_dummy", "cos_spatial", "p5", "mse", "score"):
+            assert abs(got[h][k] - want[k]) < 1e-12, (h, k)
+        assert got_labels[h] == orc.decide(want["cos_sink"], want["cos_dummy"], want["cos_spatial"], want["score"])
+        if labels[h] != D_:   # (a planted Dummy head attends to the current block either way)
+            other = orc.head_statistics(snk, dum, spa_routing, ref, gamma=0.5)
+            assert abs(other["cos_spatial"] - want["cos_spatial"]) > 1e-4, h
