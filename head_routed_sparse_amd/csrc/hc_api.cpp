@@ -320,6 +320,12 @@ int xcd_group_size(int nqt) {
 hc_status run_dense(std::vector<Entry> es, const DenseParams& base, int head_dim, int bf16, hipStream_t s,
                     int* n_items_out = nullptr) {
   std::stable_sort(es.begin(), es.end(), [](const Entry& a, const Entry& b) { return a.split_len > b.split_len; });
+  // every item must own at least one key: the kernel's step pipeline runs n >= 1 steps
+  for (const Entry& e : es)
+    if (e.nsplit < 1 || e.split_len < 1 || e.hist_len + e.cur_len < 1 ||
+        (int64_t)(e.nsplit - 1) * e.split_len >= (int64_t)e.hist_len + e.cur_len)
+      return fail(HC_ERR_STATE, "internal: dense entry of head %d has an empty key split (%d x %d over %d keys)",
+                  e.head, e.nsplit, e.split_len, e.hist_len + e.cur_len);
   int total_items = 0;
   for (size_t b0 = 0; b0 < es.size(); b0 += kMaxEntries) {
     DenseParams p = base;
@@ -562,14 +568,24 @@ hc_status hc_head_buffers_bytes(const hc_layer_desc* desc, const int32_t* labels
   return ok();
 }
 
-hc_status hc_build_head_buffers(const hc_layer_desc* desc, const int32_t* labels, const void* k_hist,
-                                const void* v_hist, int32_t n_hist_frames, void* buffer_mem,
-                                size_t buffer_bytes, hc_head_buffers** out, void* stream) {
+hc_status hc_build_head_buffers_at(const hc_layer_desc* desc, const int32_t* labels, const void* k_hist,
+                                   const void* v_hist, int32_t n_hist_frames, int64_t next_block,
+                                   void* buffer_mem, size_t buffer_bytes, hc_head_buffers** out, void* stream) {
   HC_TRY(check_desc(desc));
   HC_TRY(check_labels(*desc, labels));
   HC_TRY(check_hist_frames(*desc, n_hist_frames));
   if (!out) return fail(HC_ERR_NULL, "out is NULL");
-  const size_t need = 2 * layout(*desc, labels, nullptr, nullptr);
+  const hc_layer_desc& d = *desc;
+  const int C = d.chunk_frames;
+  const int R = rolling_blocks(d);
+  if (next_block < 0) return fail(HC_ERR_SHAPE, "next_block %lld negative", (long long)next_block);
+  // the window's history when block next_block is current: the sink block and the
+  // min(next_block - 1, R) most recent rolling blocks
+  const int64_t n_blk = (d.window_frames == C || next_block == 0) ? 0 : 1 + std::min<int64_t>(next_block - 1, R);
+  if ((int64_t)n_hist_frames != n_blk * C)
+    return fail(HC_ERR_SHAPE, "n_hist_frames %d does not match next_block %lld: the window then holds %lld frames",
+                n_hist_frames, (long long)next_block, (long long)(n_blk * C));
+  const size_t need = 2 * layout(d, labels, nullptr, nullptr);
   if (need > 0) HC_TRY(check_ptr(buffer_mem, "buffer_mem"));
   if (buffer_bytes < need) return fail(HC_ERR_WORKSPACE, "buffer_mem has %zu bytes, needs %zu", buffer_bytes, need);
   if (n_hist_frames > 0) {
@@ -579,21 +595,42 @@ hc_status hc_build_head_buffers(const hc_layer_desc* desc, const int32_t* labels
   HC_TRY(check_device());
 
   hc_head_buffers* b = new hc_head_buffers();
-  b->desc = *desc;
-  b->labels.assign(labels, labels + desc->num_heads);
+  b->desc = d;
+  b->labels.assign(labels, labels + d.num_heads);
   b->mem = (char*)buffer_mem;
   b->mem_bytes = buffer_bytes;
-  b->v_region = layout(*desc, labels, &b->head_off, &b->head_rows);
-  b->next_block = n_hist_frames / desc->chunk_frames;
+  b->v_region = layout(d, labels, &b->head_off, &b->head_rows);
+  b->next_block = next_block;
 
-  const hc_layer_desc& d = *desc;
   const int64_t S = tokens_per_frame(d);
   const size_t es_ = esize(d);
   hipStream_t s = (hipStream_t)stream;
-  // Build: the stored frames are a prefix of the logical history (block b <= R sits at
-  // position b), so each head copies one contiguous row range; a Dummy head with a
-  // buffer copies the history's last block.
-  for (int pass = 0; pass < 3 && n_hist_frames > 0; ++pass) {
+  // Logical history block i (0 = the sink block) is absolute block 0 for i = 0 and
+  // next_block - n_blk + i otherwise; block b >= 1 sits at ring position 1 + (b - 1) mod R.
+  // Sink heads keep block 0, Global and Spatial heads every block, a Dummy head with a
+  // buffer the latest one. One copy entry per (head, block).
+  std::vector<CopyEntry> copies;
+  for (int h = 0; h < d.num_heads; ++h) {
+    const int cls = b->labels[h];
+    if (b->head_off[h] < 0) continue;
+    for (int64_t i = 0; i < n_blk; ++i) {
+      int64_t pos;
+      if (cls == HC_SINK) {
+        if (i > 0) break;
+        pos = 0;
+      } else if (cls == HC_DUMMY) {
+        if (i != n_blk - 1) continue;
+        pos = 0;
+      } else {
+        const int64_t blk = i == 0 ? 0 : next_block - n_blk + i;
+        pos = blk == 0 ? 0 : 1 + (blk - 1) % R;
+      }
+      const int64_t src_row = i * C * S;
+      copies.push_back(CopyEntry{((int64_t)h * d.head_dim + src_row * d.num_heads * d.head_dim) * (int64_t)es_,
+                                 (b->head_off[h] + pos * C * S * d.head_dim) * (int64_t)es_});
+    }
+  }
+  for (size_t c0 = 0; c0 < copies.size(); c0 += kMaxEntries) {
     CopyParams p{};
     p.src_k = k_hist;
     p.src_v = v_hist;
@@ -601,29 +638,27 @@ hc_status hc_build_head_buffers(const hc_layer_desc* desc, const int32_t* labels
     p.dst_v = b->mem + b->v_region;
     p.src_stride = (int64_t)d.num_heads * d.head_dim * es_;
     p.row_bytes = d.head_dim * (int)es_;
-    const int want = pass == 0 ? HC_SINK : (pass == 1 ? HC_GLOBAL : HC_DUMMY);
-    const int64_t first_row = pass == 2 ? (int64_t)(n_hist_frames - d.chunk_frames) * S : 0;
-    int n = 0;
-    for (int h = 0; h < d.num_heads; ++h) {
-      const int cls = b->labels[h] == HC_SPATIAL ? HC_GLOBAL : b->labels[h];
-      if (b->head_off[h] < 0 || cls != want) continue;
-      p.e[n].src_off = ((int64_t)h * d.head_dim + first_row * d.num_heads * d.head_dim) * (int64_t)es_;
-      p.e[n].dst_off = b->head_off[h] * (int64_t)es_;
-      ++n;
-    }
-    p.n_entries = n;
-    p.rows = (int)(stored_frames(d, want, b->next_block) * S);
-    if (n) {
-      hipError_t e = timed(K_COPY, s, [&] { return launch_copy(p, s); });
-      if (e != hipSuccess) {
-        delete b;
-        return fail(HC_ERR_HIP, "build copy: %s", hipGetErrorString(e));
-      }
+    p.rows = (int)(C * S);
+    p.n_entries = (int)std::min(copies.size() - c0, (size_t)kMaxEntries);
+    for (int i = 0; i < p.n_entries; ++i) p.e[i] = copies[c0 + i];
+    hipError_t e = timed(K_COPY, s, [&] { return launch_copy(p, s); });
+    if (e != hipSuccess) {
+      delete b;
+      return fail(HC_ERR_HIP, "build copy: %s", hipGetErrorString(e));
     }
   }
   build_plan(b);
   *out = b;
   return ok();
+}
+
+hc_status hc_build_head_buffers(const hc_layer_desc* desc, const int32_t* labels, const void* k_hist,
+                                const void* v_hist, int32_t n_hist_frames, void* buffer_mem,
+                                size_t buffer_bytes, hc_head_buffers** out, void* stream) {
+  HC_TRY(check_desc(desc));
+  HC_TRY(check_hist_frames(*desc, n_hist_frames));
+  return hc_build_head_buffers_at(desc, labels, k_hist, v_hist, n_hist_frames, n_hist_frames / desc->chunk_frames,
+                                  buffer_mem, buffer_bytes, out, stream);
 }
 
 hc_status hc_plan_head_buffers(const hc_layer_desc* desc, const int32_t* labels, int64_t next_block,
@@ -912,8 +947,9 @@ hc_status hc_classify_heads(const hc_layer_desc* desc, const hc_classify_params*
     Entry first{(int64_t)h * D, blk, 0, h, 1, cur.split_len, base + 1};
     es.push_back(cur);
     es.push_back(first);
-    if (L.n_mid > 0) {
-      Entry mid{(int64_t)h * D + (int64_t)blk * H * D, L.n_mid * blk, 0, h, L.n_mid, cur.split_len, base + 3};
+    if (L.n_mid > 0) {   // every middle key, in n_mid ranges of split_len keys (the last one shorter)
+      const int mid_keys = (int)((int64_t)(n_hist_frames - d.chunk_frames) * S);
+      Entry mid{(int64_t)h * D + (int64_t)blk * H * D, mid_keys, 0, h, L.n_mid, cur.split_len, base + 3};
       es.push_back(mid);
     }
   }

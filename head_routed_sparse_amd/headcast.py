@@ -23,7 +23,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libheadcast.so")
+# HEADCAST_LIBRARY selects another build of the same library (the host-sanitizer build
+# of the CPU tests); either way a missing file is an error, never a fallback.
+LIB_PATH = os.environ.get("HEADCAST_LIBRARY") or os.path.join(HERE, "libheadcast.so")
 
 SINK, DUMMY, SPATIAL, GLOBAL = 0, 1, 2, 3
 HC_BF16, HC_F32 = 0, 1
@@ -65,6 +67,8 @@ _SIGS = {
     "hc_head_buffers_bytes": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _P, ctypes.POINTER(_SZ)]),
     "hc_build_head_buffers": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _P, _P, _P, _I32, _P, _SZ,
                                              ctypes.POINTER(_P), _P]),
+    "hc_build_head_buffers_at": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _P, _P, _P, _I32, _I64, _P, _SZ,
+                                                ctypes.POINTER(_P), _P]),
     "hc_plan_head_buffers": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _P, _I64, ctypes.POINTER(_P)]),
     "hc_append_chunk": (ctypes.c_int, [_P, _P, _P, _P]),
     "hc_buffers_state": (ctypes.c_int, [_P, ctypes.POINTER(_I64)]),
@@ -207,6 +211,26 @@ def hc_build_head_buffers(desc: LayerDesc, labels, k_hist, v_hist, n_hist_frames
     _check(lib().hc_build_head_buffers(ctypes.byref(desc), lab.ctypes.data_as(_P), kp, vp,
                                        int(n_hist_frames), mp, memory.numel(), ctypes.byref(h),
                                        _stream(stream)))
+    return HeadBuffers(h, memory, desc)
+
+
+def hc_build_head_buffers_at(desc: LayerDesc, labels, k_hist, v_hist, n_hist_frames: int, next_block: int,
+                             memory=None, stream=None) -> HeadBuffers:
+    """Buffers of a rollout resumed with `next_block` as the next block to append; the
+    history tensors hold the window's blocks in logical order (sink block first)."""
+    import torch
+    lab = _labels_arr(labels)
+    nbytes = hc_head_buffers_bytes(desc, lab)
+    hist = int(n_hist_frames) * desc.frame_h * desc.frame_w * desc.num_heads * desc.head_dim
+    kp = _dev(k_hist, "k_hist", _elem(desc), hist)
+    vp = _dev(v_hist, "v_hist", _elem(desc), hist)
+    if memory is None:
+        memory = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    mp = _dev(memory, "memory", torch.uint8)
+    h = _P()
+    _check(lib().hc_build_head_buffers_at(ctypes.byref(desc), lab.ctypes.data_as(_P), kp, vp,
+                                          int(n_hist_frames), int(next_block), mp, memory.numel(),
+                                          ctypes.byref(h), _stream(stream)))
     return HeadBuffers(h, memory, desc)
 
 

@@ -124,6 +124,20 @@ hc_status hc_build_head_buffers(const hc_layer_desc* desc, const int32_t* labels
                                 void* buffer_mem, size_t buffer_bytes, hc_head_buffers** out,
                                 void* stream);
 
+/* Builds the buffers of a rollout resumed at any point (Sec. 4.3 rolling overwrite):
+ * next_block is the absolute index of the block the next hc_append_chunk stores, and
+ * k_hist / v_hist hold the window's history in logical order, [n_hist_frames*S][H][d]:
+ * the sink block, then the window's rolling blocks oldest first (blocks
+ * max(1, next_block - R) .. next_block - 1). n_hist_frames must equal C times the number
+ * of those blocks (0 for next_block 0; C*(1 + min(next_block - 1, R)) otherwise), else
+ * HC_ERR_SHAPE. Each block lands at its ring position, so the handle's slot table,
+ * buffer contents and later appends are those of a handle that stored every block in
+ * turn. hc_build_head_buffers is this call with next_block = n_hist_frames / C. */
+hc_status hc_build_head_buffers_at(const hc_layer_desc* desc, const int32_t* labels, const void* k_hist,
+                                   const void* v_hist, int32_t n_hist_frames, int64_t next_block,
+                                   void* buffer_mem, size_t buffer_bytes, hc_head_buffers** out,
+                                   void* stream);
+
 /* Host-only planning handle: the same layout, ring state (next_block) and routed
  * plan as a built handle, without device memory. Only the size, state and index
  * queries accept it; append and routed calls return HC_ERR_STATE. */

@@ -228,6 +228,49 @@ def test_build_and_append_bit_exact(dtype):
     assert hc.hc_buffers_state(buf) == n_blocks
 
 
+@pytest.mark.parametrize("variant", [0, 1])
+def test_rebuild_mid_rollout_at_block_10(variant):
+    """A rollout resumed at block 10: buffers rebuilt from the window's history in
+    logical order (hc_build_head_buffers_at) equal, slot by slot and bit for bit, those of
+    a handle that stored all ten blocks in turn; both then take the same appends and
+    give bitwise-equal routed outputs, which match the oracle on the logical window."""
+    g = hin.Geometry(4, 64, 3, 5, 2, 10, 2, 2, "bf16")     # R = 3 rolling blocks
+    labels = (S_, D_, P_, G_)
+    C, S, H, d = g.chunk_frames, g.tokens_per_frame, g.num_heads, g.head_dim
+    rng = np.random.default_rng(10)
+    blocks = [hin.round_to_bf16(rng.standard_normal((3, C * S, H, d), dtype=np.float32)) for _ in range(13)]
+    desc = hc.make_desc(g, variant)
+    a = hc.hc_build_head_buffers(desc, labels, None, None, 0)
+    for b in range(10):
+        hc.hc_append_chunk(a, dev(blocks[b][1], "bf16"), dev(blocks[b][2], "bf16"))
+    hist = orc.window_history_blocks(10, g.window_frames, C)
+    kh = np.concatenate([blocks[b][1] for b in hist])
+    vh = np.concatenate([blocks[b][2] for b in hist])
+    r = hc.hc_build_head_buffers_at(desc, labels, dev(kh, "bf16"), dev(vh, "bf16"), len(hist) * C, 10)
+    ws_a, ws_r = hc.routed_workspace(a), hc.routed_workspace(r)
+    for step in range(10, 13):
+        torch.cuda.synchronize()
+        table = orc.slot_table(labels, g.window_frames, C, step, variant=variant)
+        assert np.array_equal(hc.hc_debug_slot_table(r), table)
+        assert np.array_equal(hc.hc_debug_slot_table(a), table)
+        assert hc.hc_buffers_state(r) == step
+        for h in range(H):
+            for which in ("k", "v"):
+                assert np.array_equal(buffer_rows(r, h, which), buffer_rows(a, h, which)), (step, h, which)
+        q, k, v = (dev(x, "bf16") for x in blocks[step])
+        out_a = host(hc.hc_routed_attention(a, q, k, v, workspace=ws_a))
+        out_r = host(hc.hc_routed_attention(r, q, k, v, workspace=ws_r))
+        assert np.array_equal(out_a, out_r)
+        hist = orc.window_history_blocks(step, g.window_frames, C)
+        inp = hin.LayerInputs(g, np.array(labels, np.int32), blocks[step][0],
+                              np.concatenate([blocks[b][1] for b in hist]),
+                              np.concatenate([blocks[b][2] for b in hist]), blocks[step][1], blocks[step][2],
+                              len(hist) * C)
+        assert_close(out_r, orc.routed_attention(inp, variant=variant), *TOL["bf16"], what=f"step {step}")
+        hc.hc_append_chunk(a, k, v)
+        hc.hc_append_chunk(r, k, v)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_rollout_routed_matches_oracle_window(dtype):
     """Warm-up from an empty cache, then one block per step: after every append the
@@ -258,7 +301,7 @@ def test_full_size_sampled_rows(name):
     g = inp.geom
     t = to_device(inp)
     d = hc.make_desc(g)
-    rows = sample_rows(g, n_random=192, seed=1)
+    rows = sample_rows(g, n_random=512, seed=1)
     for labels in (inp.labels, np.full(g.num_heads, G_, np.int32)):
         buf = hc.hc_build_head_buffers(d, labels, t["k_hist"], t["v_hist"], inp.n_hist_frames)
         out = host(hc.hc_routed_attention(buf, t["q"], t["k_cur"], t["v_cur"]))
@@ -318,6 +361,21 @@ def test_max_heads_routed_and_classifier_batches():
         o = ost[h]
         ref = [o["cos_sink"], o["cos_dummy"], o["cos_spatial"], o["p5"], o["mse"], o["score"]]
         assert np.allclose(stats[h], ref, atol=2e-3), (h, stats[h], ref)
+
+
+@pytest.mark.parametrize("geom", [hin.Geometry(4, 128, 10, 10, 1, 8, 3, 3, "bf16"),
+                                  hin.Geometry(4, 64, 5, 13, 1, 7, 3, 3, "bf16")])
+def test_classify_middle_blocks_not_a_tile_multiple(geom):
+    """C*S = 100 and 65 keys per block (not multiples of the 64-key tile) with 6 and 5
+    middle history frames: the reference must cover every middle key."""
+    inp = hin.generate(geom, [S_, D_, P_, G_], seed=23, planted=True)
+    got, stats = classify_gpu(inp, gamma=0.5)
+    want, ost = orc.classify_heads(inp, dict(gamma=0.5))
+    assert list(got) == list(want)
+    for h in range(4):
+        o = ost[h]
+        ref = [o["cos_sink"], o["cos_dummy"], o["cos_spatial"], o["p5"], o["mse"], o["score"]]
+        assert np.allclose(stats[h], ref, atol=3e-3), (h, stats[h], ref)
 
 
 def test_classify_unplanted_statistics_match_oracle():

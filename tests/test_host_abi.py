@@ -267,3 +267,38 @@ def test_variant_plans():
         assert n - base == (2 * 3 * g.chunk_frames * S * g.head_dim * 2 if var & 1 else 0)
     with pytest.raises(hc.HCError):
         hc.hc_head_buffers_bytes(hc.make_desc(g, 4), cfg["labels"])
+
+
+def test_build_at_block_validates_the_window_length():
+    """hc_build_head_buffers_at: the history must be exactly the window's blocks when
+    next_block is current (checked on the host, before any device call)."""
+    import ctypes
+    g = hin.Geometry(4, 64, 3, 5, 2, 10, 2, 2, "bf16")     # R = 3 rolling blocks
+    d = hc.make_desc(g)
+    L = hc.lib()
+    lab = np.array([0, 1, 2, 3], np.int32)
+    h = ctypes.c_void_p()
+    C, R = g.chunk_frames, g.window_frames // g.chunk_frames - 2
+    for nb, n_frames_ok in ((0, 0), (1, C), (3, 3 * C), (10, (1 + R) * C), (11, (1 + R) * C)):
+        for n_frames in range(0, g.hist_frames + 1, C):
+            st = L.hc_build_head_buffers_at(ctypes.byref(d), lab.ctypes.data_as(ctypes.c_void_p), ctypes.c_void_p(16),
+                                            ctypes.c_void_p(32), n_frames, nb, ctypes.c_void_p(4096), 1 << 40,
+                                            ctypes.byref(h), None)
+            if n_frames != n_frames_ok:
+                assert st == 2, (nb, n_frames, st)
+            else:   # valid arguments: only the missing device stops it here
+                assert st in (0, 7), (nb, n_frames, st)
+    st = L.hc_build_head_buffers_at(ctypes.byref(d), lab.ctypes.data_as(ctypes.c_void_p), ctypes.c_void_p(16),
+                                    ctypes.c_void_p(32), (1 + R) * C, -1, ctypes.c_void_p(4096), 1 << 40,
+                                    ctypes.byref(h), None)
+    assert st == 2
+
+
+@pytest.mark.parametrize("F,C", [(21, 3), (10, 2), (6, 3)])
+def test_resumed_plan_slot_table_at_block_10(F, C):
+    """A handle for a rollout resumed at block 10 reports the slot table of the oracle's
+    ring after ten stored blocks."""
+    g = hin.Geometry(4, 64, 3, 5, C, F, 2, 2, "bf16")
+    labels = [0, 1, 2, 3]
+    pb = hc.hc_plan_head_buffers(hc.make_desc(g), labels, 10)
+    assert np.array_equal(hc.hc_debug_slot_table(pb), orc.slot_table(labels, F, C, 10))
