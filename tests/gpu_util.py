@@ -42,14 +42,24 @@ def assert_close(got, want, max_abs, mean_abs, what=""):
 TOL = {"bf16": (1e-2, 1e-3), "f32": (1e-4, 1e-5)}
 
 
+def bf16_half_ulp(x):
+    """Half the spacing of bfloat16 (8 significant bits) around |x|: 2^(e - 8) for
+    |x| in [2^e, 2^(e + 1)); the largest error of storing x in bf16 by rounding to nearest."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return np.ldexp(1.0, (e - 8).astype(np.int64))
+
+
 def assert_close_bf16_storage(got, want, what=""):
-    """The bf16 tolerance plus the output's own storage rounding: an output of magnitude
-    |o| is stored with a half-ulp of up to 2^-8 |o|, which exceeds 1e-2 by itself once
-    |o| > 2.56 (planted heads concentrate attention on a few keys and reach |o| ~ 4)."""
+    """The bf16 tolerance (max-abs 1e-2, mean-abs 1e-3) for the kernel's own error, plus
+    the exact rounding of a bf16 output: the half-ulp at the larger of |got| and |want|
+    (planted heads concentrate attention on a few keys and reach |o| ~ 3.4, where the
+    half-ulp is 2^-7 = 7.8e-3; from |o| = 4 on it is 1.6e-2, beyond 1e-2 by itself).
+    Returns (max error, mean error, largest |want|, elements beyond the plain 1e-2)."""
     err = np.abs(got - want)
-    mag = np.abs(want)
+    room = 1e-2 + bf16_half_ulp(np.maximum(np.abs(got), np.abs(want)))
     assert np.isfinite(got).all(), f"{what}: non-finite output"
-    bad = err > 1e-2 + 2.0 ** -8 * mag
-    assert not bad.any(), f"{what}: {bad.sum()} elements beyond 1e-2 + 2^-8|o| (max err {err.max():.3e})"
-    assert err.mean() <= 1e-3 + 2.0 ** -9 * mag.mean(), f"{what}: mean-abs {err.mean():.3e}"
-    return float(err.max()), float(err.mean()), float(mag.max())
+    bad = err > room
+    assert not bad.any(), f"{what}: {bad.sum()} elements beyond 1e-2 + half-ulp (max err {err.max():.3e})"
+    assert err.mean() <= 1e-3, f"{what}: mean-abs {err.mean():.3e}"
+    return float(err.max()), float(err.mean()), float(np.abs(want).max()), int((err > 1e-2).sum())
