@@ -35,7 +35,8 @@ def parse():
     ap.add_argument("--config", default="720p", choices=["480p", "720p", "1080p"])
     ap.add_argument("--second", default="1080p", help="second workload reported beside ('' = none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=2048, help="query rows per head in the CPU sample")
+    ap.add_argument("--cpu-rows", type=int, default=None,
+                    help="query rows per head in the CPU sample of the main workload (default: CPU_ROWS)")
     ap.add_argument("--no-full-step", dest="full_step", action="store_false",
                     help="skip the 30-layer planted step")
     ap.add_argument("--labels", default="", choices=["", "global"],
@@ -145,22 +146,31 @@ def measure(name, steps, warmup, with_events, only_routed=False, labels_override
         fn = lambda: hc.hc_routed_attention(buf, q, kc, vc, out=out, workspace=ws)  # noqa: E731
         for _ in range(warmup):
             fn()
+        # timed region: K calls between two synchronisations, no events of any kind in
+        # between (the mean is `value`)
         torch.cuda.synchronize()
-        if with_events:
-            hc.hc_timing_read()
-            hc.hc_timing_enable(True)
-        # per-call durations from events on the call's stream (median and min beside the mean)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        # a second pass: events on the call's stream around each call (median, minimum)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for e0, e1 in evs:
             e0.record()
             fn()
             e1.record()
         torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) * 1e3 / steps
         call_ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
         kern = {}
         if with_events:
+            # a third pass of K calls with the library's per-kernel HIP events, recorded
+            # on the launch stream around every kernel: average duration per kernel kind
+            hc.hc_timing_read()
+            hc.hc_timing_enable(True)
+            for _ in range(steps):
+                fn()
+            torch.cuda.synchronize()
             hc.hc_timing_enable(False)
             kern = {k: (v[0] / max(v[1], 1), v[1]) for k, v in hc.hc_timing_read().items() if v[1]}
         res[tag] = dict(ms=ms, kernels=kern, labels=labels, call_median=float(np.median(call_ms)),
@@ -408,9 +418,15 @@ def full_step(steps, warmup):
             "routed_ms_per_denoise_step": round(ms, 3), "routed_ms_per_layer": round(ms / len(layers), 4)}
 
 
+# Query rows per head the CPU oracle computes for each workload's baseline: every row of
+# the 480P layer, a sample of the larger ones (each leg about 10-30 s on 16 host cores).
+CPU_ROWS = {"480p": None, "720p": 2048, "1080p": 1024}
+
+
 def cpu_baseline(inp, rows_per_head):
-    """The oracle as it stands, on a sample of query rows of every head; scaled to
-    ms per layer-step by the fraction of rows computed."""
+    """The oracle as it stands (routed step, every head), on all query rows of the layer
+    (rows_per_head None) or on a seeded sample of them, scaled to ms per layer-step by the
+    fraction of rows computed."""
     from oracle import headcast_oracle as orc
     try:
         from threadpoolctl import threadpool_info
@@ -418,15 +434,20 @@ def cpu_baseline(inp, rows_per_head):
     except Exception:
         cores = len(os.sched_getaffinity(0))
     g = inp.geom
-    rng = np.random.default_rng(0)
-    rows = np.sort(rng.choice(g.lq, size=min(rows_per_head, g.lq), replace=False))
+    if rows_per_head is None or rows_per_head >= g.lq:
+        rows = np.arange(g.lq)
+    else:
+        rng = np.random.default_rng(0)
+        rows = np.sort(rng.choice(g.lq, size=rows_per_head, replace=False))
     t0 = time.perf_counter()
     orc.routed_attention(inp, rows=rows)
     dt = time.perf_counter() - t0
     ms = dt * 1e3 * g.lq / rows.size
+    what = "all" if rows.size == g.lq else f"{rows.size} of"
     return dict(value=round(ms, 1), unit="ms/layer-step", cores=int(cores), kind="oracle",
-                sample=f"{rows.size} of {g.lq} query rows per head, all {g.num_heads} heads, "
-                       f"{g.frame_h}x{g.frame_w} layer (fp64 numpy, {dt:.1f} s), scaled by rows")
+                sample=f"{what} {g.lq} query rows per head, all {g.num_heads} heads, "
+                       f"{g.frame_h}x{g.frame_w} layer (fp64 numpy, {dt:.1f} s)"
+                       + ("" if rows.size == g.lq else ", scaled by rows"))
 
 
 def spatial_gather(g, r, n_hist, sp_flops, sp_bytes):
@@ -552,6 +573,7 @@ def main():
                            "monolithic": main_res["kv_bytes_monolithic"]},
         "context_pages_end_to_end_speedup": {"720p": 1.62, "1080p": 1.95, "hardware": "unnamed single GPU"},
     }
+    cpu_legs = {a.config: (main_res["inp"], r["ms"])}   # workload -> (inputs, GPU routed ms)
     if a.second:
         print(f"[bench] second workload {a.second}", file=sys.stderr, flush=True)
         sec = measure(a.second, max(3, a.steps // 2), 2, with_events=True)
@@ -563,6 +585,7 @@ def main():
             "dense_roofline_frac": round(dense_flops(gs, sec["routed"]["labels"], gs.hist_frames) /
                                          (sec["routed"]["kernels"]["dense"][0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "classify_ms": round(sec["classify_ms"], 3)}
+        cpu_legs[a.second] = (sec["inp"], sec["routed"]["ms"])
         del sec
     print("[bench] third workload 480p", file=sys.stderr, flush=True)
     th = measure("480p", max(3, a.steps // 2), 2, with_events=True)
@@ -574,6 +597,8 @@ def main():
         "dense_roofline_frac": round(dense_flops(gt, th["routed"]["labels"], gt.hist_frames) /
                                      (th["routed"]["kernels"]["dense"][0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "classify_ms": round(th["classify_ms"], 3)}
+    if a.config != "480p":
+        cpu_legs["480p"] = (th["inp"], th["routed"]["ms"])
     del th
     print("[bench] table-6 head mixes", file=sys.stderr, flush=True)
     out["table6_mix"] = table6_mix(max(3, a.steps // 4), 2)
@@ -587,8 +612,15 @@ def main():
         print("[bench] 30-layer step with classification", file=sys.stderr, flush=True)
         out["full_step"] = full_step(max(3, a.steps // 4), 2)
     if not a.no_cpu:
-        print("[bench] cpu oracle sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(main_res["inp"], a.cpu_rows)
+        by = {}
+        for name, (inp, gpu_ms) in cpu_legs.items():
+            print(f"[bench] cpu oracle {name}", file=sys.stderr, flush=True)
+            rows = a.cpu_rows if (name == a.config and a.cpu_rows) else CPU_ROWS[name]
+            by[name] = dict(cpu_baseline(inp, rows), gpu_routed_ms=round(gpu_ms, 4))
+            by[name]["gpu_speedup_over_oracle"] = round(by[name]["value"] / gpu_ms, 1)
+        out["cpu_baseline"] = {k: v for k, v in by[a.config].items() if k not in ("gpu_routed_ms",
+                                                                                  "gpu_speedup_over_oracle")}
+        out["cpu_baseline_by_workload"] = by
         out["cpu_context"] = cpu_context()
     print(json.dumps(out), flush=True)
 
