@@ -1112,7 +1112,7 @@ hc_status hc_debug_routed_plan(const hc_head_buffers* b, int32_t* entries, int32
       r[4] = es[i].split_len;
       r[5] = es[i].slot;
       r[6] = items;
-      r[7] = 0;
+      r[7] = kDenseQ;
     }
     items += es[i].nsplit * nqt;
   }

@@ -200,7 +200,7 @@ int32_t hc_decide(double cos_sink, double cos_dummy, double cos_spatial, double 
  * hc_debug_gather_origins: device int32 [S][2] = Spatial window origin (row, col) of
  * every position, computed by the device code the Spatial kernel uses.
  * hc_debug_routed_plan: the dense work entries of a routed call, host
- * [n][8] = {head, hist_rows, cur_rows, nsplit, split_len, slot, item_begin, 0}.
+ * [n][8] = {head, hist_rows, cur_rows, nsplit, split_len, slot, item_begin, queries per item}.
  * hc_debug_spatial_plan: the Spatial launch of a routed call, host [4] = {tile rows,
  * tile columns, frame parts, partial slots of the whole call}; zeros without Spatial
  * heads. Pure host. */

@@ -124,11 +124,13 @@ def test_routed_plan_covers_every_key_once(name, next_block):
     for lab in (labels, np.full(g.num_heads, 3, np.int32)):
         pb = hc.hc_plan_head_buffers(hc.make_desc(g), lab, next_block)
         ents, n_items = hc.hc_debug_routed_plan(pb)
-        nqt = -(-g.lq // 128)
+        qtile = int(ents[0, 7])
+        assert qtile in (128, 256) and np.all(ents[:, 7] == qtile)
+        nqt = -(-g.lq // qtile)
         hist_blocks = orc.window_history_blocks(next_block, g.window_frames, g.chunk_frames)
         assert sorted(ents[:, 0]) == list(range(g.num_heads))
         begin = 0
-        for head, hist, cur, nsplit, split_len, slot, item_begin, _ in ents:
+        for head, hist, cur, nsplit, split_len, slot, item_begin, _q in ents:
             cls = int(lab[head])
             n_hist = {0: min(len(hist_blocks), 1), 1: 0, 2: 0, 3: len(hist_blocks)}[cls]
             assert hist == n_hist * g.chunk_frames * g.tokens_per_frame
