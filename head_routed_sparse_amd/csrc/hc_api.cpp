@@ -360,6 +360,21 @@ hc_status run_dense(std::vector<Entry> es, const DenseParams& base, int head_dim
 }  // namespace
 
 // ---------------------------------------------------------------- handle
+// The launches of a routed call for the handle's current state (rebuilt only when some
+// head's stored history length changes) and the partial slots its workspace holds.
+struct Plan {
+  int64_t plan_block = -1;
+  std::vector<int32_t> plan_hist_len;
+  std::vector<Entry> entries;
+  std::vector<MergeEntry> merges;
+  std::vector<SpatialEntry> spatials;
+  int sp_parts = 1;                  // Spatial workgroups per tile (frame parts)
+  int n_slots = 0;
+  int max_slots = -1;                // partial slots the workspace provides
+  int slot_cap = -1;                 // >= 0: at most this many (the library's scratch)
+  bool ok = true;                    // false: the Spatial partials alone exceed slot_cap
+};
+
 struct hc_head_buffers {
   hc_layer_desc desc;
   std::vector<int32_t> labels;
@@ -369,16 +384,9 @@ struct hc_head_buffers {
   std::vector<int64_t> head_off;     // element offset of head rows in a region, -1 = none
   std::vector<int64_t> head_rows;    // row capacity
   int64_t next_block = 0;
-  // routed plan (rebuilt only when some head's stored history length changes)
-  int64_t plan_block = -1;
-  std::vector<int32_t> plan_hist_len;
-  std::vector<Entry> entries;
-  std::vector<MergeEntry> merges;
-  std::vector<SpatialEntry> spatials;
-  int sp_tile_r = 0, sp_tile_c = 0;   // Spatial query tile
-  int sp_parts = 1;                    // Spatial workgroups per tile (frame parts)
-  int n_slots = 0;
-  int max_slots = -1;               // partial slots the routed workspace provides
+  int sp_tile_r = 0, sp_tile_c = 0;  // Spatial query tile
+  Plan plan;                         // calls with a caller workspace
+  Plan scratch_plan;                 // the allocation-free call (slot_cap set on first use)
   bool plan_only = false;            // host-only handle (hc_plan_head_buffers)
 };
 
@@ -415,7 +423,7 @@ int64_t stored_frames(const hc_layer_desc& d, int cls, int64_t next_block) {
   return (1 + rolling) * d.chunk_frames;
 }
 
-void build_plan(hc_head_buffers* b) {
+void build_plan(hc_head_buffers* b, Plan& P) {
   const hc_layer_desc& d = b->desc;
   const int64_t S = tokens_per_frame(d);
   const int lq = (int)lq_of(d);
@@ -442,11 +450,11 @@ void build_plan(hc_head_buffers* b) {
   std::vector<int32_t> hist_len(d.num_heads);
   for (int h = 0; h < d.num_heads; ++h)
     hist_len[h] = (int32_t)(stored_frames(d, b->labels[h], b->next_block) * S);
-  if (b->plan_block >= 0 && hist_len == b->plan_hist_len) {
-    b->plan_block = b->next_block;
+  if (P.plan_block >= 0 && hist_len == P.plan_hist_len) {
+    P.plan_block = b->next_block;
     return;
   }
-  b->plan_hist_len = hist_len;
+  P.plan_hist_len = hist_len;
   // Spatial tiles and frame parts
   const bool cells = spatial_cells(d);
   int n_sp = 0;
@@ -464,21 +472,30 @@ void build_plan(hc_head_buffers* b) {
   };
   // The workspace is sized once, for the full window; every other fill state (more
   // parts never, but possibly more key splits) plans within the same slots.
-  if (b->max_slots < 0) {
+  // A capped plan (the allocation-free call) takes at most slot_cap slots: fewer key
+  // splits, and no frame parts when those do not fit.
+  if (P.max_slots < 0) {
     const int64_t full_block = 1 + rolling_blocks(d);
     int split_slots = 0;
     for (const Entry& e : make(full_block, -1))
       if (e.nsplit > 1) split_slots += e.nsplit;
-    b->max_slots = spatial_slots(parts_at(full_block)) + split_slots;
+    P.max_slots = spatial_slots(parts_at(full_block)) + split_slots;
+    if (P.slot_cap >= 0) P.max_slots = std::min(P.max_slots, P.slot_cap);
   }
-  b->sp_parts = parts_at(b->next_block);
-  const int P = b->sp_parts;
-  std::vector<Entry> es = make(b->next_block, b->max_slots - spatial_slots(P));
+  P.sp_parts = parts_at(b->next_block);
+  if (spatial_slots(P.sp_parts) > P.max_slots) P.sp_parts = 1;
+  P.ok = spatial_slots(P.sp_parts) <= P.max_slots;
+  if (!P.ok) {
+    P.plan_block = -1;   // planned again (and refused again) at the next call
+    return;
+  }
+  const int NP = P.sp_parts;
+  std::vector<Entry> es = make(b->next_block, P.max_slots - spatial_slots(NP));
   // slots: split heads and Spatial heads write fp32 partials; a Spatial head with its
   // frames in parts takes the current-block slot and one per part, merged afterwards
   int slot = 0;
-  b->merges.clear();
-  b->spatials.clear();
+  P.merges.clear();
+  P.spatials.clear();
   if (cells)
     for (int h = 0; h < d.num_heads; ++h)
       if (b->labels[h] == HC_SPATIAL) {
@@ -487,12 +504,12 @@ void build_plan(hc_head_buffers* b) {
         se.head = h;
         se.cur_slot = -1;
         se.out_slot = -1;
-        if (P > 1) {
+        if (NP > 1) {
           se.out_slot = slot;
-          b->merges.push_back(MergeEntry{h, slot, P, 0});
-          slot += P;
+          P.merges.push_back(MergeEntry{h, slot, NP, 0});
+          slot += NP;
         }
-        b->spatials.push_back(se);
+        P.spatials.push_back(se);
       }
   for (Entry& e : es) {
     const int cls = b->labels[e.head];
@@ -503,23 +520,30 @@ void build_plan(hc_head_buffers* b) {
       se.head = e.head;
       se.cur_slot = e.slot;
       se.out_slot = -1;
-      if (P > 1) {
+      if (NP > 1) {
         se.cur_slot = -1;
         se.out_slot = slot;
-        b->merges.push_back(MergeEntry{e.head, e.slot, 1 + P, 0});
-        slot += P;
+        P.merges.push_back(MergeEntry{e.head, e.slot, 1 + NP, 0});
+        slot += NP;
       }
-      b->spatials.push_back(se);
+      P.spatials.push_back(se);
     } else if (e.nsplit > 1) {
       e.slot = slot;
-      b->merges.push_back(MergeEntry{e.head, slot, e.nsplit, 0});
+      P.merges.push_back(MergeEntry{e.head, slot, e.nsplit, 0});
       slot += e.nsplit;
     }
   }
-  b->entries = es;
-  b->n_slots = slot;
-  b->plan_block = b->next_block;
-  b->max_slots = std::max(b->max_slots, slot);   // (never grows: the budget above holds)
+  P.entries = es;
+  P.n_slots = slot;
+  P.plan_block = b->next_block;
+  P.max_slots = std::max(P.max_slots, slot);   // (never grows: the budget above holds)
+  if (P.slot_cap >= 0 && slot > P.slot_cap) P.ok = false;
+}
+
+// Both plans of a handle follow its state (the capped one once it has been used).
+void update_plans(hc_head_buffers* b) {
+  build_plan(b, b->plan);
+  if (b->scratch_plan.slot_cap >= 0) build_plan(b, b->scratch_plan);
 }
 
 size_t partial_bytes(int slots, int64_t lq, int head_dim) {
@@ -647,7 +671,7 @@ hc_status hc_build_head_buffers_at(const hc_layer_desc* desc, const int32_t* lab
       return fail(HC_ERR_HIP, "build copy: %s", hipGetErrorString(e));
     }
   }
-  build_plan(b);
+  update_plans(b);
   *out = b;
   return ok();
 }
@@ -673,7 +697,7 @@ hc_status hc_plan_head_buffers(const hc_layer_desc* desc, const int32_t* labels,
   b->v_region = layout(*desc, labels, &b->head_off, &b->head_rows);
   b->next_block = next_block;
   b->plan_only = true;
-  build_plan(b);
+  update_plans(b);
   *out = b;
   return ok();
 }
@@ -717,7 +741,7 @@ hc_status hc_append_chunk(hc_head_buffers* b, const void* k_chunk, const void* v
     HC_HIP(timed(K_COPY, (hipStream_t)stream, [&] { return launch_copy(p, (hipStream_t)stream); }));
   }
   b->next_block = blk + 1;
-  build_plan(b);
+  update_plans(b);
   return ok();
 }
 
@@ -734,28 +758,34 @@ hc_status hc_free_head_buffers(hc_head_buffers* b) {
 
 hc_status hc_routed_workspace_bytes(const hc_head_buffers* b, size_t* bytes) {
   if (!b || !bytes) return fail(HC_ERR_NULL, "NULL argument");
-  *bytes = partial_bytes(b->max_slots, lq_of(b->desc), b->desc.head_dim);
+  *bytes = partial_bytes(b->plan.max_slots, lq_of(b->desc), b->desc.head_dim);
   return ok();
 }
 
-hc_status hc_routed_attention(const hc_head_buffers* b, const void* q, const void* k_cur, const void* v_cur,
-                              void* out, void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+hc_status check_routed_args(const hc_head_buffers* b, const void* q, const void* k_cur, const void* v_cur,
+                            const void* out) {
   if (!b) return fail(HC_ERR_NULL, "buffers is NULL");
   if (b->plan_only) return fail(HC_ERR_STATE, "a planning handle holds no device buffers");
   HC_TRY(check_ptr(q, "q"));
   HC_TRY(check_ptr(k_cur, "k_cur"));
   HC_TRY(check_ptr(v_cur, "v_cur"));
   HC_TRY(check_ptr(out, "out"));
+  return HC_OK;
+}
+
+// The launches of one routed call under plan P, its partial results in `workspace`
+// (at least partial_bytes(P.n_slots, ...)).
+hc_status launch_routed(const hc_head_buffers* b, const Plan& P, const void* q, const void* k_cur,
+                        const void* v_cur, void* out, void* workspace, hipStream_t s) {
   const hc_layer_desc& d = b->desc;
   const int64_t lq = lq_of(d);
-  const size_t need = partial_bytes(b->n_slots, lq, d.head_dim);
-  if (b->n_slots > 0) HC_TRY(check_ptr(workspace, "workspace"));
-  if (ws_bytes < need) return fail(HC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
-  HC_TRY(check_device());
-  hipStream_t s = (hipStream_t)stream;
   const int bf16 = d.dtype == HC_BF16;
   float* part_o = (float*)workspace;
-  float* part_ml = (float*)((char*)workspace + align_up((size_t)b->n_slots * lq * d.head_dim * 4));
+  float* part_ml = (float*)((char*)workspace + align_up((size_t)P.n_slots * lq * d.head_dim * 4));
 
   DenseParams p{};
   p.q = q;
@@ -771,9 +801,9 @@ hc_status hc_routed_attention(const hc_head_buffers* b, const void* q, const voi
   p.lq = (int)lq;
   p.nqt = ceil_div(lq, kDenseQ);
   p.scale_log2 = d.softmax_scale * 1.4426950408889634f;
-  HC_TRY(run_dense(b->entries, p, d.head_dim, bf16, s));
+  HC_TRY(run_dense(P.entries, p, d.head_dim, bf16, s));
 
-  if (!b->spatials.empty()) {
+  if (!P.spatials.empty()) {
     SpatialParams sp{};
     sp.q = q;
     sp.k_hist = b->mem;
@@ -794,16 +824,16 @@ hc_status hc_routed_attention(const hc_head_buffers* b, const void* q, const voi
     sp.tile_c = b->sp_tile_c;
     sp.tiles_r = ceil_div(d.frame_h, sp.tile_r);
     sp.tiles_c = ceil_div(d.frame_w, sp.tile_c);
-    sp.n_parts = b->sp_parts;
+    sp.n_parts = P.sp_parts;
     sp.scale_log2 = p.scale_log2;
     sp.cells = spatial_cells(d) ? 1 : 0;
     sp.k_cur = k_cur;
     sp.v_cur = v_cur;
-    sp.n_entries = (int)b->spatials.size();
-    for (size_t i = 0; i < b->spatials.size(); ++i) sp.e[i] = b->spatials[i];
+    sp.n_entries = (int)P.spatials.size();
+    for (size_t i = 0; i < P.spatials.size(); ++i) sp.e[i] = P.spatials[i];
     HC_HIP(timed(bf16 ? K_SPATIAL : K_F32, s, [&] { return launch_spatial(sp, d.head_dim, bf16, s); }));
   }
-  if (!b->merges.empty()) {
+  if (!P.merges.empty()) {
     MergeParams m{};
     m.part_o = part_o;
     m.part_ml = part_ml;
@@ -811,10 +841,50 @@ hc_status hc_routed_attention(const hc_head_buffers* b, const void* q, const voi
     m.tok_stride = p.tok_stride;
     m.lq = (int)lq;
     m.head_dim = d.head_dim;
-    m.n_entries = (int)b->merges.size();
-    for (size_t i = 0; i < b->merges.size(); ++i) m.e[i] = b->merges[i];
+    m.n_entries = (int)P.merges.size();
+    for (size_t i = 0; i < P.merges.size(); ++i) m.e[i] = P.merges[i];
     HC_HIP(timed(K_MERGE, s, [&] { return launch_merge(m, d.head_dim, bf16, s); }));
   }
+  return HC_OK;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+hc_status hc_routed_attention(const hc_head_buffers* b, const void* q, const void* k_cur, const void* v_cur,
+                              void* out, void* workspace, size_t ws_bytes, void* stream) {
+  HC_TRY(check_routed_args(b, q, k_cur, v_cur, out));
+  const size_t need = partial_bytes(b->plan.n_slots, lq_of(b->desc), b->desc.head_dim);
+  if (b->plan.n_slots > 0) HC_TRY(check_ptr(workspace, "workspace"));
+  if (ws_bytes < need) return fail(HC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  HC_TRY(check_device());
+  HC_TRY(launch_routed(b, b->plan, q, k_cur, v_cur, out, workspace, (hipStream_t)stream));
+  return ok();
+}
+
+hc_status hc_routed_attention_noalloc(hc_head_buffers* b, const void* q, const void* k_cur, const void* v_cur,
+                                      void* out, void* stream) {
+  HC_TRY(check_routed_args(b, q, k_cur, v_cur, out));
+  HC_TRY(check_device());
+  void* scratch = nullptr;
+  size_t cap = 0;
+  HC_HIP(noalloc_scratch(&scratch, &cap));
+  const hc_layer_desc& d = b->desc;
+  const int64_t lq = lq_of(d);
+  Plan& P = b->scratch_plan;
+  if (P.slot_cap < 0) {   // first call on this handle: plan within the scratch
+    int slots = (int)(cap / ((size_t)lq * (d.head_dim + 2) * 4));
+    while (slots > 0 && partial_bytes(slots, lq, d.head_dim) > cap) --slots;
+    P.slot_cap = slots;
+    build_plan(b, P);
+  }
+  if (!P.ok)
+    return fail(HC_ERR_WORKSPACE, "the Spatial heads' partial results need more than the %zu-byte scratch", cap);
+  if (partial_bytes(P.n_slots, lq, d.head_dim) > cap)
+    return fail(HC_ERR_WORKSPACE, "internal: plan of %d slots exceeds the scratch", P.n_slots);
+  HC_TRY(launch_routed(b, P, q, k_cur, v_cur, out, scratch, (hipStream_t)stream));
   return ok();
 }
 
@@ -1098,7 +1168,7 @@ hc_status hc_debug_gather_origins(const hc_layer_desc* desc, int32_t grid_h, int
 hc_status hc_debug_routed_plan(const hc_head_buffers* b, int32_t* entries, int32_t max_entries, int32_t* n_entries,
                                int32_t* n_items) {
   if (!b || !n_entries || !n_items) return fail(HC_ERR_NULL, "NULL argument");
-  std::vector<Entry> es = b->entries;
+  std::vector<Entry> es = b->plan.entries;
   std::stable_sort(es.begin(), es.end(), [](const Entry& a, const Entry& x) { return a.split_len > x.split_len; });
   const int nqt = ceil_div(lq_of(b->desc), kDenseQ);
   int items = 0;
@@ -1123,11 +1193,11 @@ hc_status hc_debug_routed_plan(const hc_head_buffers* b, int32_t* entries, int32
 
 hc_status hc_debug_spatial_plan(const hc_head_buffers* b, int32_t* plan) {
   if (!b || !plan) return fail(HC_ERR_NULL, "NULL argument");
-  const bool any = !b->spatials.empty();
+  const bool any = !b->plan.spatials.empty();
   plan[0] = any ? b->sp_tile_r : 0;
   plan[1] = any ? b->sp_tile_c : 0;
-  plan[2] = any ? b->sp_parts : 0;
-  plan[3] = b->n_slots;
+  plan[2] = any ? b->plan.sp_parts : 0;
+  plan[3] = b->plan.n_slots;
   return ok();
 }
 

@@ -2,6 +2,10 @@
 // copy (HeadCast Sec. 4.3 "Heterogeneous Cache Management": build and rolling append),
 // the classifier's per-token statistics (Sec. 4.2 Eqs. 2-4), and the fp32 variants of
 // the dense and Spatial paths used when the inputs are fp32.
+#include <mutex>
+#include <vector>
+
+#include "../../include/headcast.h"
 #include "hc_internal.h"
 #include "hc_mfma.h"
 
@@ -262,6 +266,30 @@ __global__ __launch_bounds__(64) void spatial_attn_f32(const SpatialParams p) {
 }
 
 }  // namespace
+
+// Partial results of the allocation-free routed call: one array per device, alive until
+// the process ends. Host code never uses the array's name as an address: each device's
+// copy is found with hipGetSymbolAddress (with that device current) and kept per device.
+static __device__ __align__(256) char scratch[HC_NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void** ptr, size_t* bytes) {
+  static std::mutex mu;
+  static std::vector<void*> addr;   // by device id
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = sizeof(scratch);
+  return hipSuccess;
+}
 
 hipError_t launch_merge(const MergeParams& p, int head_dim, int bf16, hipStream_t s) {
   if (p.n_entries == 0) return hipSuccess;

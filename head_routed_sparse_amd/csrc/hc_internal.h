@@ -172,4 +172,8 @@ hipError_t launch_gather_origins(int frame_h, int frame_w, int grid_h, int grid_
 
 int dense_items_grid(int n_items, int xcd_group);   // workgroups for n_items (XCD-grouped padding)
 
+// Device address and size of the library's own scratch array on the current device (the
+// partial results of the allocation-free routed call). Looked up once per device.
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
+
 }  // namespace hc

@@ -75,6 +75,7 @@ _SIGS = {
     "hc_free_head_buffers": (ctypes.c_int, [_P]),
     "hc_routed_workspace_bytes": (ctypes.c_int, [_P, ctypes.POINTER(_SZ)]),
     "hc_routed_attention": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "hc_routed_attention_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
     "hc_classify_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(LayerDesc),
                                                    ctypes.POINTER(ClassifyParams), _I32,
                                                    ctypes.POINTER(_SZ)]),
@@ -278,6 +279,21 @@ def hc_routed_attention(buffers: HeadBuffers, q, k_cur, v_cur, out=None, workspa
         workspace = routed_workspace(buffers)
     wp = _dev(workspace, "workspace", torch.uint8)
     _check(lib().hc_routed_attention(buffers.handle, qp, kp, vp, op, wp, workspace.numel(), _stream(stream)))
+    return out
+
+
+def hc_routed_attention_noalloc(buffers: HeadBuffers, q, k_cur, v_cur, out=None, stream=None):
+    """The routed step with the library's own scratch for partial results (no
+    workspace argument, no allocation in the library)."""
+    import torch
+    d, n = buffers.desc, _block_numel(buffers.desc)
+    qp = _dev(q, "q", _elem(d), n)
+    kp = _dev(k_cur, "k_cur", _elem(d), n)
+    vp = _dev(v_cur, "v_cur", _elem(d), n)
+    if out is None:
+        out = torch.empty_like(q)
+    op = _dev(out, "out", _elem(d), n)
+    _check(lib().hc_routed_attention_noalloc(buffers.handle, qp, kp, vp, op, _stream(stream)))
     return out
 
 

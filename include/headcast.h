@@ -168,6 +168,21 @@ hc_status hc_routed_attention(const hc_head_buffers* buffers, const void* q, con
                               const void* v_cur, void* out, void* workspace, size_t ws_bytes,
                               void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the routed step of
+ * hc_routed_attention with its partial results in a scratch array that the library
+ * keeps on every device it runs on (HC_NOALLOC_SCRATCH_BYTES, held until the process
+ * ends) instead of a caller workspace. It calls no allocation routine. On a handle's
+ * first such call the library plans its launches within the scratch (fewer key splits
+ * than hc_routed_attention may use when they do not fit; same outputs up to rounding
+ * order); HC_ERR_WORKSPACE if the Spatial heads' partials alone exceed the scratch.
+ * All calls on one device share the scratch: calls that overlap in time on one device
+ * (several streams or host threads) race and must be ordered by the caller. Contents
+ * need no initialisation. */
+#define HC_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+hc_status hc_routed_attention_noalloc(hc_head_buffers* buffers, const void* q, const void* k_cur,
+                                      const void* v_cur, void* out, void* stream);
+
 /* ---------------------------------------------------------------- classification (Sec. 4.2)
  * One-time classification over the full window: the reference output (Eq. 2) and the
  * Sink / Dummy / Spatial proxy outputs in fp32, per-token cosines against the
