@@ -305,20 +305,68 @@ int spatial_parts(const hc_layer_desc& d, int tile_r, int tile_c, int n_sp, int 
   return (int)std::max<int64_t>(1, std::min<int64_t>({free_x, kMaxSpParts, n_frames}));
 }
 
-// Items of one key range (its query tiles) are dispatched consecutively; keeping a
-// run of them on one XCD lets them share the key range through that XCD's L2.
-int xcd_group_size(int nqt) {
-  static int forced = [] {
-    const char* e = getenv("HC_XCD_GROUP");
-    return e ? atoi(e) : 0;
-  }();
-  if (forced > 0) return forced;
-  return std::max(1, std::min(nqt, kXcdGroup));
+// XCD queues of one dense launch. A group is the query tiles of one key range (one split
+// of one entry); its tiles read the same keys, which an XCD's L2 fetches once for all of
+// them. Each class of equally long items (the groups of one split length, in logical
+// order) is dealt to the 8 XCDs in 8 contiguous, equal parts: every XCD then runs the
+// same mix of item lengths, longest first, on its 64 workgroup slots (the packing of a
+// deal of single items), while a group spans only the XCDs its part boundaries cross.
+// If some queue would need more than kXcdRuns runs, each XCD takes one contiguous block
+// of items instead.
+struct ItemGroup {
+  int first, count;
+  double cost;   // per item, in key tiles
+};
+
+void plan_xcd_queues(DenseParams& p, std::vector<ItemGroup> gs) {
+  std::stable_sort(gs.begin(), gs.end(), [](const ItemGroup& a, const ItemGroup& b) { return a.cost > b.cost; });
+  std::vector<XcdRun> q[kXcds];
+  auto add = [&](int x, int f, int c) {
+    if (c <= 0) return;
+    if (!q[x].empty() && q[x].back().first + q[x].back().count == f)
+      q[x].back().count += c;
+    else
+      q[x].push_back(XcdRun{f, c});
+  };
+  for (size_t c0 = 0; c0 < gs.size();) {
+    size_t c1 = c0;
+    int n = 0;
+    while (c1 < gs.size() && gs[c1].cost == gs[c0].cost) n += gs[c1++].count;
+    // items of the class in order: position t lies in group g at tile t - start(g)
+    int start = 0;
+    for (size_t g = c0; g < c1; ++g) {
+      const int a = start, b = start + gs[g].count;
+      for (int x = 0; x < kXcds; ++x) {
+        const int lo = (int)((int64_t)n * x / kXcds), hi = (int)((int64_t)n * (x + 1) / kXcds);
+        const int f = std::max(a, lo), e = std::min(b, hi);
+        add(x, gs[g].first + (f - a), e - f);
+      }
+      start = b;
+    }
+    c0 = c1;
+  }
+  bool fits = true;
+  for (int x = 0; x < kXcds; ++x) fits = fits && (int)q[x].size() <= kXcdRuns;
+  if (!fits) {
+    for (int x = 0; x < kXcds; ++x) {
+      const int b0 = (int)((int64_t)p.n_items * x / kXcds), b1 = (int)((int64_t)p.n_items * (x + 1) / kXcds);
+      q[x].assign(1, XcdRun{b0, b1 - b0});
+    }
+  }
+  p.xcd_len = 0;
+  for (int x = 0; x < kXcds; ++x) {
+    int len = 0;
+    p.xcd_nrun[x] = (int)q[x].size();
+    for (size_t r = 0; r < q[x].size(); ++r) {
+      p.xcd_run[x][r] = q[x][r];
+      len += q[x][r].count;
+    }
+    p.xcd_len = std::max(p.xcd_len, len);
+  }
 }
 
-// Launch dense entries (batched by kMaxEntries), longest items first.
-hc_status run_dense(std::vector<Entry> es, const DenseParams& base, int head_dim, int bf16, hipStream_t s,
-                    int* n_items_out = nullptr) {
+// Launch parameters of dense entries (batched by kMaxEntries), longest items first.
+hc_status dense_launches(std::vector<Entry> es, const DenseParams& base, std::vector<DenseParams>* out) {
   std::stable_sort(es.begin(), es.end(), [](const Entry& a, const Entry& b) { return a.split_len > b.split_len; });
   // every item must own at least one key: the kernel's step pipeline runs n >= 1 steps
   for (const Entry& e : es)
@@ -326,11 +374,12 @@ hc_status run_dense(std::vector<Entry> es, const DenseParams& base, int head_dim
         (int64_t)(e.nsplit - 1) * e.split_len >= (int64_t)e.hist_len + e.cur_len)
       return fail(HC_ERR_STATE, "internal: dense entry of head %d has an empty key split (%d x %d over %d keys)",
                   e.head, e.nsplit, e.split_len, e.hist_len + e.cur_len);
-  int total_items = 0;
+  out->clear();
   for (size_t b0 = 0; b0 < es.size(); b0 += kMaxEntries) {
     DenseParams p = base;
     const size_t n = std::min(es.size() - b0, (size_t)kMaxEntries);
     int items = 0;
+    std::vector<ItemGroup> groups;
     for (size_t i = 0; i < n; ++i) {
       const Entry& e = es[b0 + i];
       DenseEntry& d = p.e[i];
@@ -343,17 +392,27 @@ hc_status run_dense(std::vector<Entry> es, const DenseParams& base, int head_dim
       d.slot = e.slot;
       d.item_begin = items;
       d.pad = 0;
+      const int total = e.hist_len + e.cur_len;
+      for (int sp = 0; sp < e.nsplit; ++sp) {
+        const int len = std::min(e.split_len, total - sp * e.split_len);
+        groups.push_back(ItemGroup{items + sp * base.nqt, base.nqt, len / (double)kKeyTile + kItemOverheadTiles});
+      }
       items += e.nsplit * base.nqt;
     }
     p.n_entries = (int)n;
     p.n_items = items;
-    p.xcd_group = xcd_group_size(base.nqt);
-    total_items += items;
-    if (!n_items_out) {
-      HC_HIP(timed(bf16 ? K_DENSE : K_F32, s, [&] { return launch_dense(p, head_dim, bf16, s); }));
-    }
+    plan_xcd_queues(p, groups);
+    out->push_back(p);
   }
-  if (n_items_out) *n_items_out = total_items;
+  return HC_OK;
+}
+
+// Launch dense entries.
+hc_status run_dense(const std::vector<Entry>& es, const DenseParams& base, int head_dim, int bf16, hipStream_t s) {
+  std::vector<DenseParams> ps;
+  HC_TRY(dense_launches(es, base, &ps));
+  for (const DenseParams& p : ps)
+    HC_HIP(timed(bf16 ? K_DENSE : K_F32, s, [&] { return launch_dense(p, head_dim, bf16, s); }));
   return HC_OK;
 }
 
@@ -1188,6 +1247,28 @@ hc_status hc_debug_routed_plan(const hc_head_buffers* b, int32_t* entries, int32
   }
   *n_entries = (int32_t)es.size();
   *n_items = items;
+  return ok();
+}
+
+hc_status hc_debug_dense_queues(const hc_head_buffers* b, int32_t* runs, int32_t* n_runs, int32_t* queue_len) {
+  if (!b || !runs || !n_runs || !queue_len) return fail(HC_ERR_NULL, "NULL argument");
+  DenseParams base{};
+  base.lq = (int)lq_of(b->desc);
+  base.nqt = ceil_div(base.lq, kDenseQ);
+  std::vector<DenseParams> ps;
+  HC_TRY(dense_launches(b->plan.entries, base, &ps));
+  for (int x = 0; x < kXcds; ++x) n_runs[x] = 0;
+  *queue_len = 0;
+  if (ps.empty()) return ok();
+  const DenseParams& p = ps[0];
+  for (int x = 0; x < kXcds; ++x) {
+    n_runs[x] = p.xcd_nrun[x];
+    for (int r = 0; r < kXcdRuns; ++r) {
+      runs[(x * kXcdRuns + r) * 2] = r < p.xcd_nrun[x] ? p.xcd_run[x][r].first : -1;
+      runs[(x * kXcdRuns + r) * 2 + 1] = r < p.xcd_nrun[x] ? p.xcd_run[x][r].count : 0;
+    }
+  }
+  *queue_len = p.xcd_len;
   return ok();
 }
 

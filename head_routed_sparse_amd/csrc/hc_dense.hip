@@ -5,9 +5,9 @@
 // One workgroup = 128 queries of one head against one key range: a split of the
 // head's [history rows ; current-block rows]. History rows come from the compact
 // per-head buffer (stride D) or, for the classifier, from the monolithic cache
-// (stride H*D); current-block rows are read in place from [C*S][H][D]. Items are
-// ordered longest first and grouped per XCD so that the query tiles sharing a key
-// range run on the same L2.
+// (stride H*D); current-block rows are read in place from [C*S][H][D]. Items run from
+// per-XCD queues (planned on the host) that keep the query tiles of one key range on
+// one XCD, so that they share the range through its L2, each queue longest first.
 //
 // A workgroup is four waves of 32 queries (one per SIMD, all state in VGPRs). For D=128
 // two workgroups share a CU, each with its own LDS ring and barrier, so that one's
@@ -32,8 +32,18 @@ void dense_attn_bf16(const DenseParams p) {
   __shared__ __attribute__((aligned(1024))) char ring[NS * R::kStageBytes];
   lds_char* const lds = (lds_char*)ring;
 
-  const int item = xcd_logical(blockIdx.x, p.xcd_group);
-  if (item >= p.n_items) return;
+  // this workgroup's item: position blockIdx.x / 8 of the queue of XCD blockIdx.x % 8
+  const int xq = blockIdx.x % kXcds;
+  int k = blockIdx.x / kXcds;
+  int item = -1;
+  for (int r = 0; r < p.xcd_nrun[xq]; ++r) {
+    if (k < p.xcd_run[xq][r].count) {
+      item = p.xcd_run[xq][r].first + k;
+      break;
+    }
+    k -= p.xcd_run[xq][r].count;
+  }
+  if (item < 0) return;
   int ei = 0;
   while (ei + 1 < p.n_entries && item >= p.e[ei + 1].item_begin) ++ei;
   const DenseEntry e = p.e[ei];
@@ -151,18 +161,13 @@ void dense_attn_bf16(const DenseParams p) {
 
 }  // namespace
 
-int dense_items_grid(int n_items, int xcd_group) {
-  const int span = 8 * xcd_group;
-  return (n_items + span - 1) / span * span;
-}
-
 hipError_t launch_dense_f32(const DenseParams& p, int head_dim, hipStream_t s);
 
 hipError_t launch_dense(const DenseParams& p, int head_dim, int bf16, hipStream_t s) {
   if (p.n_items == 0) return hipSuccess;
   if (!bf16) return launch_dense_f32(p, head_dim, s);
   // four waves of 32 queries for both head sizes
-  const dim3 grid(dense_items_grid(p.n_items, p.xcd_group));
+  const dim3 grid(kXcds * p.xcd_len);
   if (head_dim == 64)
     hipLaunchKernelGGL((dense_attn_bf16<64, 1>), grid, dim3(64 * (kDenseQ / 32)), 0, s, p);
   else

@@ -9,7 +9,8 @@ namespace hc {
 constexpr int kMaxEntries = 64;   // dense work entries per launch (kernel arguments by value)
 constexpr int kKeyTile = 64;      // granularity of key-range splits (a multiple of the 32-key step)
 constexpr int kDenseQ = 128;      // queries per dense workgroup (query tile)
-constexpr int kXcdGroup = 8;      // consecutive items (same key range) kept on one XCD
+constexpr int kXcds = 8;          // XCDs; workgroup i is dispatched to XCD i % 8, in order i / 8
+constexpr int kXcdRuns = 16;      // runs of consecutive items in one XCD's queue
 constexpr int kSpTileMax = 32;    // positions per Spatial query tile (one 32-query MFMA block)
 
 // First row (or column) of the g-wide Spatial window around pos in a frame of `extent`
@@ -44,6 +45,12 @@ struct DenseEntry {
   int32_t pad;
 };
 
+// Items [first, first + count) of one dense launch, run in order by one XCD.
+struct XcdRun {
+  int32_t first;
+  int32_t count;
+};
+
 struct DenseParams {
   const void* q;         // [lq][H][D]
   const void* k_hist;    // history rows, row stride hist_stride elements
@@ -60,8 +67,10 @@ struct DenseParams {
   int32_t n_entries;
   int32_t n_items;
   float scale_log2;      // softmax_scale * log2(e)
-  int32_t xcd_group;     // consecutive items kept on one XCD
+  int32_t xcd_len;       // workgroups of each XCD's queue (grid = kXcds * xcd_len)
   DenseEntry e[kMaxEntries];
+  int32_t xcd_nrun[kXcds];           // runs in each XCD's queue
+  XcdRun xcd_run[kXcds][kXcdRuns];   // queue x = the items of its runs, in order
 };
 
 // Merge of partial slots into the normalised output (split keys, Spatial merge).
@@ -170,7 +179,6 @@ hipError_t launch_stats(const StatsParams& p, hipStream_t s);
 hipError_t launch_gather_origins(int frame_h, int frame_w, int grid_h, int grid_w, int cells, int32_t* out,
                                  hipStream_t s);
 
-int dense_items_grid(int n_items, int xcd_group);   // workgroups for n_items (XCD-grouped padding)
 
 // Device address and size of the library's own scratch array on the current device (the
 // partial results of the allocation-free routed call). Looked up once per device.

@@ -61,16 +61,6 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);   // a.hi | b.hi << 16
 }
 
-// Work item -> logical index, keeping runs of kXcdGroup consecutive logical items on
-// one XCD (workgroups are dispatched round-robin over the 8 XCDs) while the overall
-// dispatch order still follows the logical order.
-__device__ __forceinline__ int xcd_logical(int bid, int group) {
-  const int span = 8 * group;
-  const int base = (bid / span) * span;
-  const int within = bid % span;
-  return base + (within % 8) * group + within / 8;
-}
-
 // Workgroup id -> logical index in [0, total) such that the workgroups of one XCD
 // (ids x, x + 8, x + 16, ...) take one contiguous block of logical indices.
 __device__ __forceinline__ int xcd_block(int bid, int total) {

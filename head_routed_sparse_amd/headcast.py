@@ -89,6 +89,7 @@ _SIGS = {
                                             ctypes.POINTER(_I64)]),
     "hc_debug_gather_origins": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _I32, _I32, _P, _P]),
     "hc_debug_routed_plan": (ctypes.c_int, [_P, _P, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
+    "hc_debug_dense_queues": (ctypes.c_int, [_P, _P, _P, ctypes.POINTER(_I32)]),
     "hc_debug_spatial_plan": (ctypes.c_int, [_P, _P]),
     "hc_timing_enable": (ctypes.c_int, [_I32]),
     "hc_timing_read": (ctypes.c_int, [_P, _P]),
@@ -366,6 +367,17 @@ def hc_debug_routed_plan(buffers: HeadBuffers):
     _check(lib().hc_debug_routed_plan(buffers.handle, e.ctypes.data_as(_P), n.value, ctypes.byref(n),
                                       ctypes.byref(items)))
     return e, items.value
+
+
+def hc_debug_dense_queues(buffers: HeadBuffers):
+    """XCD queues of the routed call's dense launch: a list of 8 lists of (first, count)
+    runs, and the longest queue."""
+    runs = np.zeros((8, 16, 2), np.int32)
+    n = np.zeros(8, np.int32)
+    ln = _I32()
+    _check(lib().hc_debug_dense_queues(buffers.handle, runs.ctypes.data_as(_P), n.ctypes.data_as(_P),
+                                       ctypes.byref(ln)))
+    return [[tuple(int(v) for v in runs[x, r]) for r in range(n[x])] for x in range(8)], ln.value
 
 
 def hc_debug_spatial_plan(buffers: HeadBuffers):

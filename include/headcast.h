@@ -162,7 +162,8 @@ hc_status hc_free_head_buffers(hc_head_buffers* buffers); /* host handle only */
  * the Spatial heads' current-block part and history frame parts); its contents need no
  * initialisation. The size covers every fill state of the handle's window. Output
  * dtype = input dtype. Calls on one handle are ordered by their streams; calls that
- * share a workspace must not overlap. */
+ * share a workspace must not overlap. (The workspace argument is this library's
+ * addition to the step's inputs: the library allocates no device memory.) */
 hc_status hc_routed_workspace_bytes(const hc_head_buffers* buffers, size_t* bytes);
 hc_status hc_routed_attention(const hc_head_buffers* buffers, const void* q, const void* k_cur,
                               const void* v_cur, void* out, void* workspace, size_t ws_bytes,
@@ -189,7 +190,10 @@ hc_status hc_routed_attention_noalloc(hc_head_buffers* buffers, const void* q, c
  * reference, their means (Eq. 3), the Spatial score P_pct(cos) - gamma * MSE (Eq. 4)
  * and the decision of Eq. 5. Requires n_hist_frames >= C (the sink block present).
  * Synchronises `stream`. labels_out: host [H]; stats_out (nullable): host [H][6] =
- * {cos_sink, cos_dummy, cos_spatial, p_pct, mse, score}. */
+ * {cos_sink, cos_dummy, cos_spatial, p_pct, mse, score}, in double because the host
+ * reduces the per-token values in fp64; the percentile and MSE are returned beside the
+ * score so that each part of Eq. 4 can be checked. n_hist_frames: the frames the history
+ * tensors hold (classification may run before the window is full). */
 hc_status hc_classify_workspace_bytes(const hc_layer_desc* desc, const hc_classify_params* params,
                                       int32_t n_hist_frames, size_t* bytes);
 hc_status hc_classify_heads(const hc_layer_desc* desc, const hc_classify_params* params,
@@ -213,9 +217,13 @@ int32_t hc_decide(double cos_sink, double cos_dummy, double cos_spatial, double 
  * hc_debug_head_region: byte offsets of head h's K and V rows inside buffer_mem and
  * its row capacity (-1 / 0 for a head without buffer); pure host.
  * hc_debug_gather_origins: device int32 [S][2] = Spatial window origin (row, col) of
- * every position, computed by the device code the Spatial kernel uses.
+ * every position for a grid_h x grid_w window (the classifier's proxy window may differ
+ * from the routing grid), computed on `stream` by the device code the Spatial kernel uses.
  * hc_debug_routed_plan: the dense work entries of a routed call, host
  * [n][8] = {head, hist_rows, cur_rows, nsplit, split_len, slot, item_begin, queries per item}.
+ * hc_debug_dense_queues: the XCD queues of the routed call's (first) dense launch: host
+ * runs [8][16][2] = {first item, items} (-1 / 0 past n_runs[x]), n_runs [8], and the
+ * longest queue; workgroup i runs on XCD i % 8, taking position i / 8 of its queue.
  * hc_debug_spatial_plan: the Spatial launch of a routed call, host [4] = {tile rows,
  * tile columns, frame parts, partial slots of the whole call}; zeros without Spatial
  * heads. Pure host. */
@@ -226,6 +234,8 @@ hc_status hc_debug_gather_origins(const hc_layer_desc* desc, int32_t grid_h, int
                                   void* r0c0, void* stream);
 hc_status hc_debug_routed_plan(const hc_head_buffers* buffers, int32_t* entries, int32_t max_entries,
                                int32_t* n_entries, int32_t* n_items);
+hc_status hc_debug_dense_queues(const hc_head_buffers* buffers, int32_t* runs, int32_t* n_runs,
+                                int32_t* queue_len);
 hc_status hc_debug_spatial_plan(const hc_head_buffers* buffers, int32_t* plan);
 
 /* ---------------------------------------------------------------- timing

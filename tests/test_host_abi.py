@@ -304,3 +304,47 @@ def test_resumed_plan_slot_table_at_block_10(F, C):
     labels = [0, 1, 2, 3]
     pb = hc.hc_plan_head_buffers(hc.make_desc(g), labels, 10)
     assert np.array_equal(hc.hc_debug_slot_table(pb), orc.slot_table(labels, F, C, 10))
+
+
+@pytest.mark.parametrize("name", ["tiny", "480p", "720p", "1080p"])
+@pytest.mark.parametrize("global_only", [False, True])
+def test_dense_xcd_queues_cover_items_balanced_longest_first(name, global_only):
+    """The dense launch's per-XCD queues hold every item exactly once, each queue runs
+    longest items first, every XCD gets an equal share (within one item) of every class
+    of equally long items, and a key-range group spans few XCDs."""
+    cfg = hin.CONFIGS[name]
+    g = cfg["geom"]
+    labels = np.full(g.num_heads, 3, np.int32) if global_only else cfg["labels"]
+    pb = hc.hc_plan_head_buffers(hc.make_desc(g), labels, 7)
+    ents, n_items = hc.hc_debug_routed_plan(pb)
+    queues, qlen = hc.hc_debug_dense_queues(pb)
+    nqt = -(-g.lq // int(ents[0, 7]))
+    cost = np.zeros(n_items)
+    group = np.zeros(n_items, np.int64)
+    for head, hist, cur, nsplit, split_len, slot, item_begin, _q in ents:
+        for sp in range(nsplit):
+            lo = item_begin + sp * nqt
+            cost[lo:lo + nqt] = min(split_len, hist + cur - sp * split_len) / 64 + 3.0
+            group[lo:lo + nqt] = lo
+    seen = np.zeros(n_items, np.int64)
+    per_class = {}
+    spans = {}
+    for x, q in enumerate(queues):
+        assert len(q) <= 16
+        items = [f + i for f, c in q for i in range(c)]
+        seen[items] += 1
+        assert all(cost[a] >= cost[b] for a, b in zip(items, items[1:]))
+        for c in set(cost[items]):
+            per_class.setdefault(c, []).append(int(np.sum(cost[items] == c)))
+        for i in items:
+            spans.setdefault(group[i], set()).add(x)
+    assert np.all(seen == 1)
+    assert qlen == max(sum(c for _, c in q) for q in queues)
+    for c, counts in per_class.items():
+        counts += [0] * (8 - len(counts))
+        assert max(counts) - min(counts) <= 1, (c, counts)
+    # groups of a class with at least 8 groups' worth of items span at most 3 XCDs
+    n_groups = {c: len({group[i] for i in range(n_items) if cost[i] == c}) for c in per_class}
+    for gid, xs in spans.items():
+        if n_groups[cost[gid]] >= 8:
+            assert len(xs) <= 3, (gid, xs)
