@@ -8,29 +8,38 @@
 // position share the key set exactly; with three chunk frames the fourth wave only
 // loads). It walks the union of the tile's windows in 32-key steps, chunk-outer and
 // frame-inner, on the dense kernel's pipeline (hc_pipe.h): every step's rows are
-// gathered whole (256 B) by 16-byte direct loads into the LDS ring. The union position
-// of every row a lane loads, and every lane's window bits, depend only on the chunk, so
-// they are computed once per chunk; the window mask is folded into the exponent's
-// addend (-inf outside the window). With frame parts, each of n_parts workgroups walks
-// its share of the frames and stores an fp32 partial that the merge kernel joins. In
-// final mode the result is merged with the dense current-block partial by its
-// log-sum-exp and written as bf16; in partial mode (classifier, frame parts) it is
-// stored as fp32; with cells the whole key set is walked here.
+// gathered whole (256 B) by 16-byte direct loads into the LDS ring. The token of every
+// row a step loads, and every lane's window bits, depend only on the chunk: for unions
+// of up to kTblChunks chunks the workgroup writes them to two small LDS tables once, and
+// each lane reads its entries when a chunk starts (larger unions work them out there).
+// The window mask is folded into the exponent's addend (-inf outside the window), which
+// changes only with the chunk and the reference max. With frame parts, each of n_parts
+// workgroups walks its share of the frames and stores an fp32 partial that the merge
+// kernel joins. In final mode the result is merged with the dense current-block partial
+// by its log-sum-exp and written as bf16; in partial mode (classifier, frame parts) it
+// is stored as fp32; with cells the whole key set is walked here.
 #include "hc_pipe.h"
 
 namespace hc {
 
 namespace {
 
-template <int D>
+// Unions of up to this many 32-key chunks keep their per-chunk tables in LDS.
+constexpr int kTblChunks = 8;
+
+template <int D, bool TABLE>
 __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams p) {
   constexpr int W = 4;
   using R = Ring<D, 1, W>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int NS = 4;   // ring stages
-  __shared__ __attribute__((aligned(1024))) char ring[NS * R::kStageBytes];
+  constexpr int kTokBytes = TABLE ? kTblChunks * kStep * 4 : 0;
+  constexpr int kBitBytes = TABLE ? kTblChunks * 64 * 2 : 0;
+  __shared__ __attribute__((aligned(1024))) char ring[NS * R::kStageBytes + kTokBytes + kBitBytes];
   lds_char* const lds = (lds_char*)ring;
+  lds_char* const tok_tbl = lds + NS * R::kStageBytes;   // int32 [chunk][row of the step]
+  lds_char* const bit_tbl = tok_tbl + kTokBytes;         // uint16 [chunk][lane]
 
   // the tiles of one XCD are neighbours (same head, same frames), so the L2 keeps the
   // window rows they share
@@ -70,8 +79,6 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
   const int half = lane >> 5;
   const int pr = R0 + l32 / p.tile_c, pc = C0 + l32 % p.tile_c;
   const bool pos_ok = l32 < p.tile_r * p.tile_c && pr < fh && pc < fw;
-  const int r0q = org_r(min(pr, fh - 1)), ehq = ext_r(min(pr, fh - 1));
-  const int c0q = org_c(min(pc, fw - 1)), ewq = ext_c(min(pc, fw - 1));
 
   const char* kh = (const char*)p.k_hist + e.hist_off * 2;
   const char* vh = (const char*)p.v_hist + e.hist_off * 2;
@@ -87,6 +94,39 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
     const int q = i / UW;
     return (ur0 + q) * fw + uc0 + (i - q * UW);
   };
+  // window bits of lane ln's 16 keys in union chunk cu: bit 4 a + b for key 8 a + 4 (ln / 32) + b
+  auto chunk_bits = [&](int cu, int ln) {
+    const int q32 = ln & 31, hf = ln >> 5;
+    const int qr = R0 + q32 / p.tile_c, qc = C0 + q32 % p.tile_c;
+    const int r0l = org_r(min(qr, fh - 1)), ehl = ext_r(min(qr, fh - 1));
+    const int c0l = org_c(min(qc, fw - 1)), ewl = ext_c(min(qc, fw - 1));
+    uint32_t b16 = 0;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int i0 = cu * kStep + 8 * a + 4 * hf;
+      int ur = i0 / UW, uc = i0 - ur * UW;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const bool in = i0 + b < nU && (unsigned)(ur0 + ur - r0l) < (unsigned)ehl &&
+                        (unsigned)(uc0 + uc - c0l) < (unsigned)ewl;
+        b16 |= (uint32_t)in << (4 * a + b);
+        if (++uc == UW) {
+          uc = 0;
+          ++ur;
+        }
+      }
+    }
+    return b16;
+  };
+  // the per-chunk data: the token of each row a step loads, and each lane's window bits
+  // (written once per workgroup; larger unions work them out when a chunk starts)
+  if (TABLE) {
+    for (int x = tid; x < nchunk * kStep; x += 256)
+      *(__attribute__((address_space(3))) int*)(tok_tbl + 4 * x) = union_tok(x);
+    for (int x = tid; x < nchunk * 64; x += 256)
+      *(__attribute__((address_space(3))) uint16_t*)(bit_tbl + 2 * x) = (uint16_t)chunk_bits(x / 64, x % 64);
+    __syncthreads();
+  }
 
   for (int cf0 = 0; cf0 < p.chunk_frames; cf0 += W) {
     const int cf = cf0 + wave;
@@ -98,13 +138,17 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) q[0][ks] = *(const u32x4*)(qp + ks * 16 + half * 8);
 
-    // loads: step t = chunk t / n_frames of the union in frame t % n_frames, issued in order
+    // loads: step t = chunk t / n_frames of the union in frame f0 + t % n_frames, issued
+    // in order
     int iu = 0, ifr = 0;
     int tok[R::kLoads];
     auto issue = [&](int, int stage) {
-      if (ifr == 0) {
+      if (ifr == 0) {   // a new chunk: the tokens of this lane's rows
 #pragma unroll
-        for (int i = 0; i < R::kLoads; ++i) tok[i] = union_tok(iu * kStep + la.ld_row[i]);
+        for (int i = 0; i < R::kLoads; ++i) {
+          const int row = iu * kStep + la.ld_row[i];
+          tok[i] = TABLE ? *(const __attribute__((address_space(3))) int*)(tok_tbl + 4 * row) : union_tok(row);
+        }
       }
       const int fr = f0 + ifr;
       const bool cur = fr >= nh;
@@ -138,23 +182,9 @@ __global__ __launch_bounds__(256, 2) void spatial_attn_bf16(const SpatialParams 
       for (int r = 0; r < 16; ++r) add[r] = (bits >> r) & 1u ? -blk[0].m : -INFINITY;
     };
     auto prep = [&]() {
-      if (mf == 0) {
-        bits = 0;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int i0 = mu * kStep + 8 * a + 4 * half;
-          int ur = i0 / UW, uc = i0 - ur * UW;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const bool in = i0 + b < nU && (unsigned)(ur0 + ur - r0q) < (unsigned)ehq &&
-                            (unsigned)(uc0 + uc - c0q) < (unsigned)ewq;
-            bits |= (uint32_t)in << (4 * a + b);
-            if (++uc == UW) {
-              uc = 0;
-              ++ur;
-            }
-          }
-        }
+      if (mf == 0) {   // a new chunk
+        bits = TABLE ? *(const __attribute__((address_space(3))) uint16_t*)(bit_tbl + 2 * (mu * 64 + lane))
+                     : chunk_bits(mu, lane);
         refresh();
       }
       if (++mf == n_frames) {
@@ -232,10 +262,35 @@ hipError_t launch_spatial(const SpatialParams& p, int head_dim, int bf16, hipStr
   if (p.n_entries == 0) return hipSuccess;
   if (!bf16) return launch_spatial_f32(p, head_dim, s);
   const dim3 grid(p.tiles_r * p.tiles_c * p.n_parts * p.n_entries), block(256);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(spatial_attn_bf16<128>, grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL(spatial_attn_bf16<64>, grid, block, 0, s, p);
+  // the largest union of a tile's windows (rows and columns vary independently)
+  int ur = 0, uc = 0;
+  const bool cells = p.cells != 0;
+  for (int r0 = 0; r0 < p.frame_h; r0 += p.tile_r) {
+    const int r1 = std::min(r0 + p.tile_r, p.frame_h) - 1;
+    const int lo = cells ? cell_origin(r0, p.grid_h) : win_origin(r0, p.grid_h, p.frame_h);
+    const int hi = cells ? cell_origin(r1, p.grid_h) + cell_extent(r1, p.grid_h, p.frame_h)
+                         : win_origin(r1, p.grid_h, p.frame_h) + std::min(p.grid_h, p.frame_h);
+    ur = std::max(ur, hi - lo);
+  }
+  for (int c0 = 0; c0 < p.frame_w; c0 += p.tile_c) {
+    const int c1 = std::min(c0 + p.tile_c, p.frame_w) - 1;
+    const int lo = cells ? cell_origin(c0, p.grid_w) : win_origin(c0, p.grid_w, p.frame_w);
+    const int hi = cells ? cell_origin(c1, p.grid_w) + cell_extent(c1, p.grid_w, p.frame_w)
+                         : win_origin(c1, p.grid_w, p.frame_w) + std::min(p.grid_w, p.frame_w);
+    uc = std::max(uc, hi - lo);
+  }
+  const bool table = (ur * uc + kStep - 1) / kStep <= kTblChunks;
+  if (head_dim == 128) {
+    if (table)
+      hipLaunchKernelGGL((spatial_attn_bf16<128, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((spatial_attn_bf16<128, false>), grid, block, 0, s, p);
+  } else {
+    if (table)
+      hipLaunchKernelGGL((spatial_attn_bf16<64, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((spatial_attn_bf16<64, false>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 
