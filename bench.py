@@ -111,6 +111,38 @@ def measured_traffic(workload):
     return rec["traffic_bytes_per_launch"]
 
 
+def dense_plan(hc, buf, geom):
+    """Load balance of the routed call's dense launch as planned: every item (one query
+    tile against one key split) costs its 32-key steps; each XCD's queue is dealt in
+    order to its 64 workgroup slots (32 CUs x 2), each item to the slot that frees
+    first. Returns the total steps, the longest slot (makespan) and the balance
+    total / (512 x makespan): the fraction of slot time the plan keeps busy."""
+    import heapq
+    ents, n_items = hc.hc_debug_routed_plan(buf)
+    if n_items == 0:
+        return None
+    cost = np.zeros(n_items, np.int64)
+    for head, hist, cur, nsplit, split_len, slot, begin, qtile in ents:
+        nqt = -(-geom.lq // int(qtile))
+        total = int(hist) + int(cur)
+        for s in range(int(nsplit)):
+            ln = min(int(split_len), total - s * int(split_len))
+            cost[int(begin) + s * nqt:int(begin) + (s + 1) * nqt] = -(-ln // 32)
+    queues, _ = hc.hc_debug_dense_queues(buf)
+    slots_per_xcd = 64 if geom.head_dim == 128 else 128
+    makespan = total = items = 0
+    for runs in queues:
+        heap = [0] * slots_per_xcd
+        for first, count in runs:
+            for i in range(first, first + count):
+                heapq.heapreplace(heap, heap[0] + int(cost[i]))
+                total += int(cost[i])
+                items += 1
+        makespan = max(makespan, max(heap))
+    return {"items": items, "steps_total": total, "makespan_steps": int(makespan),
+            "balance": round(total / (8 * slots_per_xcd * makespan), 4)}
+
+
 def time_calls(fn, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -174,7 +206,8 @@ def measure(name, steps, warmup, with_events, only_routed=False, labels_override
             hc.hc_timing_enable(False)
             kern = {k: (v[0] / max(v[1], 1), v[1]) for k, v in hc.hc_timing_read().items() if v[1]}
         res[tag] = dict(ms=ms, kernels=kern, labels=labels, call_median=float(np.median(call_ms)),
-                        call_min=float(call_ms.min()), spatial_plan=hc.hc_debug_spatial_plan(buf))
+                        call_min=float(call_ms.min()), spatial_plan=hc.hc_debug_spatial_plan(buf),
+                        dense_plan=dense_plan(hc, buf, g))
         del buf, ws, out
     res["geom"] = g
     res["inp"] = inp
@@ -558,6 +591,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(a.config),
                      "kernel": "dense_attn_bf16<128, 1>", "flops_per_launch": dflops},
+        "dense_plan": dict(r["dense_plan"], kernel_us_per_makespan_step=round(dense_ms * 1e3 / r["dense_plan"]["makespan_steps"], 4),
+                           frac_at_full_balance=round(achieved / PEAK_BF16_TFLOPS / r["dense_plan"]["balance"], 4)),
         "full_window_roofline_frac": round(dense_flops(g, base["labels"], n_hist) /
                                            (base["kernels"]["dense"][0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "spatial_gather": spatial_gather(g, r, n_hist, sp_flops, sp_bytes),
@@ -584,6 +619,7 @@ def main():
             "speedup_vs_full_window": round(sec["all_global"]["ms"] / sec["routed"]["ms"], 3),
             "dense_roofline_frac": round(dense_flops(gs, sec["routed"]["labels"], gs.hist_frames) /
                                          (sec["routed"]["kernels"]["dense"][0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "dense_plan": sec["routed"]["dense_plan"],
             "classify_ms": round(sec["classify_ms"], 3)}
         cpu_legs[a.second] = (sec["inp"], sec["routed"]["ms"])
         del sec
@@ -596,6 +632,7 @@ def main():
         "speedup_vs_full_window": round(th["all_global"]["ms"] / th["routed"]["ms"], 3),
         "dense_roofline_frac": round(dense_flops(gt, th["routed"]["labels"], gt.hist_frames) /
                                      (th["routed"]["kernels"]["dense"][0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "dense_plan": th["routed"]["dense_plan"],
         "classify_ms": round(th["classify_ms"], 3)}
     if a.config != "480p":
         cpu_legs["480p"] = (th["inp"], th["routed"]["ms"])

@@ -169,13 +169,20 @@ constexpr int kNumCu = 256;
 // Dense workgroups resident per CU: d = 128 fills half the LDS and registers with two,
 // d = 64 (a 32 KB ring, 119 registers) takes four.
 int dense_slots(int head_dim) { return kNumCu * (head_dim == 64 ? 4 : kSlotsPerCu); }
-constexpr double kItemOverheadTiles = 3.0;
+// Fixed cost of one dense item (query loads, ring fill, epilogue), in key tiles: fitted
+// to the measured times of two plans of the 480P-shaped layer (888 and 1443 items).
+constexpr double kItemOverheadTiles = 9.0;
+// The merge of key-split partials in key-tile units of the dense makespan: a dense
+// workgroup takes about 1.8 us per 64-key tile (128 queries, d = 128) and the merge
+// kernel reads partials at about 3.9 TB/s, so one tile of time reads about 7 MB.
+constexpr double kMergeBytesPerTile = 7e6;
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 // Makespan estimate (in key tiles) of LPT list scheduling of the entries' items on
-// n_slots workgroup slots; items run in order of decreasing length.
-double lpt_makespan(const std::vector<Entry>& es, int nqt, int n_slots) {
+// n_slots workgroup slots; items run in order of decreasing length. Stops early, with
+// a value above `cutoff`, once the makespan passes it.
+double lpt_makespan(const std::vector<Entry>& es, int nqt, int n_slots, double cutoff = 1e300) {
   std::vector<std::pair<double, int64_t>> items;   // (cost, count)
   for (const Entry& e : es) {
     const int total = e.hist_len + e.cur_len;
@@ -195,41 +202,118 @@ double lpt_makespan(const std::vector<Entry>& es, int nqt, int n_slots) {
       slots.pop();
       slots.push(t);
       makespan = std::max(makespan, t);
+      if (makespan > cutoff) return makespan;
     }
   return makespan;
 }
 
-// Choose one key-split length for all entries (a multiple of the key tile): the
-// candidate with the smallest estimated makespan; splitting only when it pays. A
-// split entry takes one partial slot per split; candidates needing more than
-// slot_budget such slots are skipped (< 0: no limit; one split per entry always fits).
-// n_slots: dense workgroups the GPU runs at once.
-void plan_splits(std::vector<Entry>& es, int nqt, int slot_budget, int n_slots) {
+// Key splits of the entries: each class of equally long entries (all Global heads, all
+// Sink heads, ...) is cut into k pieces of one length (a multiple of the key tile), k
+// chosen for the smallest estimated time; splitting only when it pays. The search
+// starts from the best length common to all classes and then improves one class at a
+// time (each class: k = 1..16, kept when the makespan drops). A split entry takes one
+// partial slot per piece; choices needing more than slot_budget such slots are skipped
+// (< 0: no limit; no splits always fits). n_slots: dense workgroups the GPU runs at once.
+// The estimate adds the merge of the pieces' fp32 partials (piece_bytes each).
+void plan_splits_search(std::vector<Entry>& es, int nqt, int slot_budget, int n_slots, double piece_bytes) {
   auto apply = [](Entry& e, int len) {
     const int total = e.hist_len + e.cur_len;
     e.nsplit = e.whole ? 1 : std::max(1, ceil_div(total, len));
     e.split_len = std::max(kKeyTile, ceil_div(ceil_div(std::max(total, 1), e.nsplit), kKeyTile) * kKeyTile);
   };
-  int max_total = 0;
-  for (const Entry& e : es) max_total = std::max(max_total, e.hist_len + e.cur_len);
+  auto piece = [](int total, int k) { return ceil_div(ceil_div(std::max(total, 1), k), kKeyTile) * kKeyTile; };
+  // classes: the distinct lengths of the entries that may be split
+  std::vector<int> totals;
+  for (const Entry& e : es)
+    if (!e.whole) totals.push_back(e.hist_len + e.cur_len);
+  std::sort(totals.begin(), totals.end(), std::greater<int>());
+  totals.erase(std::unique(totals.begin(), totals.end()), totals.end());
+  if (totals.empty() || totals[0] == 0) {
+    for (Entry& e : es) apply(e, std::max(totals.empty() ? 1 : totals[0], 1));
+    return;
+  }
+  // cost of a choice (pieces per class): estimated makespan plus the merge of the
+  // pieces' partials; negative when the partial slots do not fit the budget
+  std::vector<int> k(totals.size(), 1);
   double best = -1;
-  int best_len = std::max(max_total, 1);
-  for (int k = 1; k <= 16 && max_total > 0; ++k) {
-    const int len = ceil_div(ceil_div(max_total, k), kKeyTile) * kKeyTile;
+  auto cost = [&](const std::vector<int>& kk) {
     std::vector<Entry> trial = es;
-    int slots = 0;
+    int slots = 0, extra = 0;
     for (Entry& e : trial) {
-      apply(e, len);
+      if (e.whole) {
+        apply(e, e.hist_len + e.cur_len);
+        continue;
+      }
+      const int c = (int)(std::find(totals.begin(), totals.end(), e.hist_len + e.cur_len) - totals.begin());
+      apply(e, piece(totals[c], kk[c]));
       if (e.nsplit > 1) slots += e.nsplit;
     }
-    if (slot_budget >= 0 && slots > slot_budget && k > 1) continue;
-    const double m = lpt_makespan(trial, nqt, n_slots) * (1.0 + 0.01 * (k - 1));   // mild bias to fewer splits
-    if (best < 0 || m < best) {
+    for (int x : kk) extra += x - 1;
+    if (slot_budget >= 0 && slots > slot_budget && extra > 0) return -1.0;
+    const double bias = 1.0 + 0.001 * extra;   // ties go to fewer pieces
+    const double merge = slots * piece_bytes / kMergeBytesPerTile;
+    return (lpt_makespan(trial, nqt, n_slots, best < 0 ? 1e300 : best / bias - merge) + merge) * bias;
+  };
+  // common length first (k pieces of the longest entry)
+  for (int kl = 1; kl <= 16; ++kl) {
+    const int len = piece(totals[0], kl);
+    std::vector<int> kk(totals.size());
+    for (size_t c = 0; c < totals.size(); ++c) kk[c] = std::max(1, ceil_div(totals[c], len));
+    const double m = cost(kk);
+    if (m >= 0 && (best < 0 || m < best)) {
       best = m;
-      best_len = len;
+      k = kk;
     }
   }
-  for (Entry& e : es) apply(e, best_len);
+  // then one class at a time
+  for (int round = 0; round < 3; ++round) {
+    bool moved = false;
+    for (size_t c = 0; c < totals.size(); ++c)
+      for (int kc = 1; kc <= 16; ++kc) {
+        if (kc == k[c]) continue;
+        std::vector<int> kk = k;
+        kk[c] = kc;
+        const double m = cost(kk);
+        if (m >= 0 && m < best * 0.999) {
+          best = m;
+          k = kk;
+          moved = true;
+        }
+      }
+    if (!moved) break;
+  }
+  for (Entry& e : es) {
+    if (e.whole) {
+      apply(e, e.hist_len + e.cur_len);
+      continue;
+    }
+    const int c = (int)(std::find(totals.begin(), totals.end(), e.hist_len + e.cur_len) - totals.begin());
+    apply(e, piece(totals[c], k[c]));
+  }
+}
+
+void plan_splits(std::vector<Entry>& es, int nqt, int slot_budget, int n_slots, int64_t piece_bytes) {
+  // decisions are kept per input (layers of one geometry and head mix plan alike)
+  static std::mutex mu;
+  static std::map<std::vector<int64_t>, std::vector<std::pair<int, int>>> memo;
+  std::vector<int64_t> key{nqt, slot_budget, n_slots, piece_bytes};
+  for (const Entry& e : es) key.push_back(((int64_t)(e.hist_len + e.cur_len) << 1) | (e.whole ? 1 : 0));
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = memo.find(key);
+    if (it != memo.end()) {
+      for (size_t i = 0; i < es.size(); ++i) {
+        es[i].nsplit = it->second[i].first;
+        es[i].split_len = it->second[i].second;
+      }
+      return;
+    }
+  }
+  plan_splits_search(es, nqt, slot_budget, n_slots, (double)piece_bytes);
+  std::vector<std::pair<int, int>> val;
+  for (const Entry& e : es) val.push_back({e.nsplit, e.split_len});
+  std::lock_guard<std::mutex> lk(mu);
+  memo[key] = val;
 }
 
 // Spatial query tile (tile_r x tile_c positions, 24..32 of them): the shape with the
@@ -501,7 +585,7 @@ void build_plan(hc_head_buffers* b, Plan& P) {
       e.whole = cls == HC_SPATIAL;
       es.push_back(e);
     }
-    plan_splits(es, nqt, slot_budget, dense_slots(d.head_dim));
+    plan_splits(es, nqt, slot_budget, dense_slots(d.head_dim), (int64_t)lq * (d.head_dim + 2) * 4);
     return es;
   };
   // the plan depends on the state only through the stored history lengths, which stop
