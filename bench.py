@@ -483,6 +483,43 @@ def cpu_baseline(inp, rows_per_head):
                        + ("" if rows.size == g.lq else ", scaled by rows"))
 
 
+def planted_accuracy(layer=29, rows_per_head=512):
+    """The oracle on one layer of the planted 30-layer 720P workload (the seeded numpy
+    recipe), timed on a row sample like cpu_baseline, and compared on the same rows with
+    the GPU: classification of the layer, then the routed step with the GPU's labels.
+    Planted heads reach |o| ~ 3.4, where storing a bf16 output alone rounds by up to
+    7.8e-3; the figures are reported against the plain 1e-2."""
+    import torch
+    from oracle import headcast_oracle as orc
+    from head_routed_sparse_amd import headcast as hc
+    from head_routed_sparse_amd import inputs as hin
+    inp = hin.full_step_layer_inputs("full720p", layer)
+    g = inp.geom
+
+    def dev(a):
+        return torch.from_numpy(a).to(torch.bfloat16).cuda()
+
+    q, kh, vh, kc, vc = (dev(a) for a in (inp.q, inp.k_hist, inp.v_hist, inp.k_cur, inp.v_cur))
+    desc = hc.make_desc(g)
+    labels, _ = hc.hc_classify_heads(desc, hc.hc_default_classify_params(gamma=0.5), q, kh, vh, inp.n_hist_frames,
+                                     kc, vc)
+    buf = hc.hc_build_head_buffers(desc, labels, kh, vh, inp.n_hist_frames)
+    got = hc.hc_routed_attention(buf, q, kc, vc).float().cpu().numpy()
+    rng = np.random.default_rng(layer)
+    rows = np.sort(rng.choice(g.lq, size=rows_per_head, replace=False))
+    t0 = time.perf_counter()
+    want = orc.routed_attention(inp, labels=labels, rows=rows)
+    dt = time.perf_counter() - t0
+    err = np.abs(got[rows].astype(np.float64) - want)
+    return {"workload": f"planted 30-layer 720P workload, layer {layer} (numpy recipe), {rows.size} random rows "
+                        f"per head, labels from the GPU classification",
+            "labels_equal_planted": bool(np.array_equal(labels, inp.labels)),
+            "max_abs": float(f"{err.max():.4g}"), "mean_abs": float(f"{err.mean():.3g}"),
+            "max_abs_output": float(f"{np.abs(want).max():.3g}"),
+            "elements_over_1e-2": int((err > 1e-2).sum()), "elements": int(err.size),
+            "oracle_seconds": round(dt, 1)}
+
+
 def spatial_gather(g, r, n_hist, sp_flops, sp_bytes):
     """The Spatial kernel against HBM (unique bytes) and against the matrix cores (the
     flops it issues, union steps included)."""
@@ -658,6 +695,8 @@ def main():
         out["cpu_baseline"] = {k: v for k, v in by[a.config].items() if k not in ("gpu_routed_ms",
                                                                                   "gpu_speedup_over_oracle")}
         out["cpu_baseline_by_workload"] = by
+        print("[bench] planted layer against the oracle", file=sys.stderr, flush=True)
+        out["planted_accuracy"] = planted_accuracy()
         out["cpu_context"] = cpu_context()
     print(json.dumps(out), flush=True)
 

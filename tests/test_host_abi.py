@@ -145,6 +145,49 @@ def test_routed_plan_covers_every_key_once(name, next_block):
         assert list(ents[:, 4]) == sorted(ents[:, 4], reverse=True)
 
 
+def planned_balance(pb, g):
+    """Sum of the items' 32-key steps over 512 slots x the longest slot, each XCD's queue
+    dealt in order to its 64 slots (32 CUs x 2 workgroups), each item to the slot that
+    frees first."""
+    import heapq
+    ents, n_items = hc.hc_debug_routed_plan(pb)
+    nqt = -(-g.lq // int(ents[0, 7]))
+    cost = np.zeros(n_items, np.int64)
+    for head, hist, cur, nsplit, split_len, slot, begin, _q in ents:
+        for s in range(nsplit):
+            cost[begin + s * nqt:begin + (s + 1) * nqt] = -(-min(split_len, hist + cur - s * split_len) // 32)
+    queues, _ = hc.hc_debug_dense_queues(pb)
+    span = 0
+    for q in queues:
+        heap = [0] * 64
+        for first, count in q:
+            for i in range(first, first + count):
+                heapq.heapreplace(heap, heap[0] + int(cost[i]))
+        span = max(span, max(heap))
+    return cost.sum() / (512 * span)
+
+
+@pytest.mark.parametrize("name,floor", [("480p", 0.85), ("720p", 0.95), ("1080p", 0.99)])
+def test_key_splits_per_class_and_planned_balance(name, floor):
+    """The split search decides per class of equally long entries: entries of one length
+    share one piece count and one piece length (a multiple of the key tile, no empty
+    piece), and the dense launch of the full window keeps its slots busy (planned balance
+    at least `floor`, routed and all-Global)."""
+    cfg = hin.CONFIGS[name]
+    g = cfg["geom"]
+    for lab in (cfg["labels"], np.full(g.num_heads, 3, np.int32)):
+        pb = hc.hc_plan_head_buffers(hc.make_desc(g), lab, g.window_frames // g.chunk_frames - 1)
+        ents, _ = hc.hc_debug_routed_plan(pb)
+        by_len = {}
+        for head, hist, cur, nsplit, split_len, slot, begin, _q in ents:
+            total = int(hist + cur)
+            assert split_len % 64 == 0 and (nsplit - 1) * split_len < total <= nsplit * split_len
+            if lab[head] != 2:   # a Spatial head's current block is never split
+                by_len.setdefault(total, set()).add((int(nsplit), int(split_len)))
+        assert all(len(v) == 1 for v in by_len.values()), by_len
+        assert planned_balance(pb, g) >= floor
+
+
 @pytest.mark.parametrize("name", ["tiny", "480p", "720p", "1080p"])
 @pytest.mark.parametrize("variant", [0, 1, 2, 3])
 def test_routed_workspace_fits_every_fill_state(name, variant):
