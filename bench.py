@@ -88,7 +88,7 @@ def spatial_mfma_flops(geom, n_sp, n_hist, tile_r, tile_c):
     return 4.0 * 32 * 32 * geom.head_dim * steps * n_hist * geom.chunk_frames * n_sp
 
 
-KERNEL_SOURCES = ["hc_dense.hip", "hc_pipe.h", "hc_mfma.h", "hc_internal.h"]
+KERNEL_SOURCES = ["hc_dense.hip", "hc_spatial_tile.h", "hc_pipe.h", "hc_mfma.h", "hc_internal.h"]
 COUNTERS = os.path.join(ROOT, "profiles", "dense_attn_bf16_720p_counters.json")
 
 
@@ -111,23 +111,48 @@ def measured_traffic(workload):
     return rec["traffic_bytes_per_launch"]
 
 
-def dense_plan(hc, buf, geom):
+def spatial_item_steps(geom, tile_r, tile_c, parts):
+    """32-key steps of the Spatial items of one head in launch order (frame part by
+    frame part, tile by tile): the union of a tile's windows in whole steps, in every
+    frame of the part."""
+    fh, fw, gh, gw = geom.frame_h, geom.frame_w, geom.grid_h, geom.grid_w
+
+    def org(p, g, ext):
+        return min(max(p - g // 2, 0), max(ext - g, 0))
+
+    steps = []
+    for r0 in range(0, fh, tile_r):
+        r1 = min(r0 + tile_r, fh) - 1
+        ur = org(r1, gh, fh) + min(gh, fh) - org(r0, gh, fh)
+        for c0 in range(0, fw, tile_c):
+            c1 = min(c0 + tile_c, fw) - 1
+            uc = org(c1, gw, fw) + min(gw, fw) - org(c0, gw, fw)
+            steps.append(-(-ur * uc // 32))
+    nh = geom.hist_frames
+    return [c * ((i + 1) * nh // parts - i * nh // parts) for i in range(parts) for c in steps]
+
+
+def dense_plan(hc, buf, geom, labels):
     """Load balance of the routed call's dense launch as planned: every item (one query
-    tile against one key split) costs its 32-key steps; each XCD's queue is dealt in
-    order to its 64 workgroup slots (32 CUs x 2), each item to the slot that frees
-    first. Returns the total steps, the longest slot (makespan) and the balance
-    total / (512 x makespan): the fraction of slot time the plan keeps busy."""
+    tile against one key split, or one Spatial tile when those run in the launch) costs
+    its 32-key steps; each XCD's queue is dealt in order to its 64 workgroup slots
+    (32 CUs x 2), each item to the slot that frees first. Returns the total steps, the
+    longest slot (makespan) and the balance total / (512 x makespan): the fraction of
+    slot time the plan keeps busy."""
     import heapq
     ents, n_items = hc.hc_debug_routed_plan(buf)
     if n_items == 0:
         return None
-    cost = np.zeros(n_items, np.int64)
+    cost = []
     for head, hist, cur, nsplit, split_len, slot, begin, qtile in ents:
         nqt = -(-geom.lq // int(qtile))
         total = int(hist) + int(cur)
         for s in range(int(nsplit)):
-            ln = min(int(split_len), total - s * int(split_len))
-            cost[int(begin) + s * nqt:int(begin) + (s + 1) * nqt] = -(-ln // 32)
+            cost += [-(-min(int(split_len), total - s * int(split_len)) // 32)] * nqt
+    tr, tc, parts, _, fused = hc.hc_debug_spatial_plan(buf)
+    if fused:
+        cost += spatial_item_steps(geom, tr, tc, parts) * int(np.sum(np.asarray(labels) == 2))
+    cost = np.array(cost, np.int64)
     queues, _ = hc.hc_debug_dense_queues(buf)
     slots_per_xcd = 64 if geom.head_dim == 128 else 128
     makespan = total = items = 0
@@ -140,7 +165,7 @@ def dense_plan(hc, buf, geom):
                 items += 1
         makespan = max(makespan, max(heap))
     return {"items": items, "steps_total": total, "makespan_steps": int(makespan),
-            "balance": round(total / (8 * slots_per_xcd * makespan), 4)}
+            "balance": round(total / (8 * slots_per_xcd * makespan), 4), "spatial_tiles_in_launch": bool(fused)}
 
 
 def time_calls(fn, steps, warmup):
@@ -155,7 +180,16 @@ def time_calls(fn, steps, warmup):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
-def measure(name, steps, warmup, with_events, only_routed=False, labels_override=""):
+def launch_flops(geom, r, n_hist):
+    """Algorithmic flops of a routed call's dense launch: the dense paths, plus the
+    Spatial path's history part when its tiles run in the same launch."""
+    fl = dense_flops(geom, r["labels"], n_hist)
+    if r["spatial_plan"][4]:
+        fl += spatial_work(geom, r["labels"], n_hist)[0]
+    return fl
+
+
+def measure(name, steps, warmup, with_events, only_routed=False, labels_override="", variant=0):
     import torch
     from head_routed_sparse_amd import headcast as hc
     from head_routed_sparse_amd import inputs as hin
@@ -166,7 +200,7 @@ def measure(name, steps, warmup, with_events, only_routed=False, labels_override
         return torch.from_numpy(a).to(torch.bfloat16).cuda()
 
     q, kh, vh, kc, vc = (dev(a) for a in (inp.q, inp.k_hist, inp.v_hist, inp.k_cur, inp.v_cur))
-    desc = hc.make_desc(g)
+    desc = hc.make_desc(g, variant)
     res = {}
     runs = [("routed", np.full(g.num_heads, 3, np.int32) if labels_override == "global" else inp.labels)]
     if not only_routed:
@@ -207,7 +241,7 @@ def measure(name, steps, warmup, with_events, only_routed=False, labels_override
             kern = {k: (v[0] / max(v[1], 1), v[1]) for k, v in hc.hc_timing_read().items() if v[1]}
         res[tag] = dict(ms=ms, kernels=kern, labels=labels, call_median=float(np.median(call_ms)),
                         call_min=float(call_ms.min()), spatial_plan=hc.hc_debug_spatial_plan(buf),
-                        dense_plan=dense_plan(hc, buf, g))
+                        dense_plan=dense_plan(hc, buf, g, labels))
         del buf, ws, out
     res["geom"] = g
     res["inp"] = inp
@@ -526,7 +560,7 @@ def spatial_gather(g, r, n_hist, sp_flops, sp_bytes):
     if "spatial" not in r["kernels"]:
         return None
     ms = r["kernels"]["spatial"][0]
-    tile_r, tile_c, parts, _ = r["spatial_plan"]
+    tile_r, tile_c, parts, _, _ = r["spatial_plan"]
     n_sp = int((np.asarray(r["labels"]) == 2).sum())
     mf = spatial_mfma_flops(g, n_sp, n_hist, tile_r, tile_c)
     return {"flops": sp_flops, "unique_bytes": sp_bytes, "avg_ms": round(ms, 4),
@@ -590,15 +624,21 @@ def main():
         dense_ms = r["kernels"]["dense"][0]
         print(json.dumps({"workload": a.config, "routed_ms": round(r["ms"], 4),
                           "kernel_avg_ms": {k: round(v[0], 4) for k, v in r["kernels"].items()},
-                          "dense_tflops": round(dense_flops(g, r["labels"], g.hist_frames) / (dense_ms * 1e-3) / 1e12, 1)}),
+                          "dense_tflops": round(launch_flops(g, r, g.hist_frames) / (dense_ms * 1e-3) / 1e12, 1)}),
               flush=True)
         return
     n_hist = g.hist_frames
     r, base = main_res["routed"], main_res["all_global"]
     dense_ms = r["kernels"]["dense"][0]
-    dflops = dense_flops(g, r["labels"], n_hist)
+    dflops = launch_flops(g, r, n_hist)
+    fused = bool(r["spatial_plan"][4])
     achieved = dflops / (dense_ms * 1e-3) / 1e12
     sp_flops, sp_bytes = spatial_work(g, r["labels"], n_hist)
+    # the same call with the Spatial path in its own launch: that kernel alone against
+    # its roofline, and the routed step in that form
+    print("[bench] Spatial path in its own launch", file=sys.stderr, flush=True)
+    own = measure(a.config, max(3, a.steps // 2), 2, with_events=True, only_routed=True,
+                  variant=hc.HC_VARIANT_SPATIAL_OWN_LAUNCH)["routed"]
     out = {
         "metric": METRIC,
         "value": round(r["ms"], 4),
@@ -627,12 +667,15 @@ def main():
         "full_window_kernel_avg_ms": {k: round(v[0], 4) for k, v in base["kernels"].items()},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(a.config),
-                     "kernel": "dense_attn_bf16<128, 1>", "flops_per_launch": dflops},
+                     "kernel": "dense_spatial_bf16<true>" if fused else "dense_attn_bf16<128, 1>",
+                     "spatial_tiles_in_launch": fused, "flops_per_launch": dflops},
         "dense_plan": dict(r["dense_plan"], kernel_us_per_makespan_step=round(dense_ms * 1e3 / r["dense_plan"]["makespan_steps"], 4),
                            frac_at_full_balance=round(achieved / PEAK_BF16_TFLOPS / r["dense_plan"]["balance"], 4)),
         "full_window_roofline_frac": round(dense_flops(g, base["labels"], n_hist) /
                                            (base["kernels"]["dense"][0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "spatial_gather": spatial_gather(g, r, n_hist, sp_flops, sp_bytes),
+        "spatial_gather": spatial_gather(g, own, n_hist, sp_flops, sp_bytes),
+        "spatial_own_launch": {"routed_ms": round(own["ms"], 4),
+                               "kernel_avg_ms": {k: round(v[0], 4) for k, v in own["kernels"].items()}},
         "copies": {"build_bytes": main_res["build_bytes"], "build_kernel_ms": round(main_res["build_kernel_ms"], 4),
                    "build_hbm_frac": round(main_res["build_bytes"] / (main_res["build_kernel_ms"] * 1e-3) / 1e9 /
                                            PEAK_HBM_GBS, 4),
@@ -654,7 +697,7 @@ def main():
             "workload": a.second, "routed_ms": round(sec["routed"]["ms"], 4),
             "full_window_ms": round(sec["all_global"]["ms"], 4),
             "speedup_vs_full_window": round(sec["all_global"]["ms"] / sec["routed"]["ms"], 3),
-            "dense_roofline_frac": round(dense_flops(gs, sec["routed"]["labels"], gs.hist_frames) /
+            "dense_roofline_frac": round(launch_flops(gs, sec["routed"], gs.hist_frames) /
                                          (sec["routed"]["kernels"]["dense"][0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "dense_plan": sec["routed"]["dense_plan"],
             "classify_ms": round(sec["classify_ms"], 3)}
@@ -667,7 +710,7 @@ def main():
         "workload": "480p", "routed_ms": round(th["routed"]["ms"], 4),
         "full_window_ms": round(th["all_global"]["ms"], 4),
         "speedup_vs_full_window": round(th["all_global"]["ms"] / th["routed"]["ms"], 3),
-        "dense_roofline_frac": round(dense_flops(gt, th["routed"]["labels"], gt.hist_frames) /
+        "dense_roofline_frac": round(launch_flops(gt, th["routed"], gt.hist_frames) /
                                      (th["routed"]["kernels"]["dense"][0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "dense_plan": th["routed"]["dense_plan"],
         "classify_ms": round(th["classify_ms"], 3)}

@@ -75,7 +75,8 @@ hc_status check_desc(const hc_layer_desc* d) {
     return fail(HC_ERR_SHAPE, "window_frames %d must be a positive multiple of chunk_frames %d",
                 d->window_frames, d->chunk_frames);
   if (d->grid_h < 1 || d->grid_w < 1) return fail(HC_ERR_SHAPE, "grid %dx%d must be >= 1", d->grid_h, d->grid_w);
-  if (d->variant < 0 || d->variant > (HC_VARIANT_DUMMY_PREVIOUS | HC_VARIANT_SPATIAL_CELLS))
+  if (d->variant < 0 ||
+      d->variant > (HC_VARIANT_DUMMY_PREVIOUS | HC_VARIANT_SPATIAL_CELLS | HC_VARIANT_SPATIAL_OWN_LAUNCH))
     return fail(HC_ERR_SHAPE, "variant %d unknown", d->variant);
   if (!(d->softmax_scale > 0.f) || !std::isfinite(d->softmax_scale))
     return fail(HC_ERR_SHAPE, "softmax_scale must be positive and finite");
@@ -179,6 +180,10 @@ constexpr double kMergeBytesPerTile = 7e6;
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
+// Cost (in key tiles) of one dense item: its keys, the fixed cost, and the partial of a
+// split entry.
+double item_cost(int len, int nsplit) { return len / (double)kKeyTile + kItemOverheadTiles + (nsplit > 1 ? 1.0 : 0.0); }
+
 // Makespan estimate (in key tiles) of LPT list scheduling of the entries' items on
 // n_slots workgroup slots; items run in order of decreasing length. Stops early, with
 // a value above `cutoff`, once the makespan passes it.
@@ -187,9 +192,7 @@ double lpt_makespan(const std::vector<Entry>& es, int nqt, int n_slots, double c
   for (const Entry& e : es) {
     const int total = e.hist_len + e.cur_len;
     for (int s = 0; s < e.nsplit; ++s) {
-      const int len = std::min(e.split_len, total - s * e.split_len);
-      const double cost = len / (double)kKeyTile + kItemOverheadTiles + (e.nsplit > 1 ? 1.0 : 0.0);
-      items.push_back({cost, nqt});
+      items.push_back({item_cost(std::min(e.split_len, total - s * e.split_len), e.nsplit), nqt});
     }
   }
   std::sort(items.begin(), items.end(), [](auto& a, auto& b) { return a.first > b.first; });
@@ -321,6 +324,22 @@ void plan_splits(std::vector<Entry>& es, int nqt, int slot_budget, int n_slots, 
 // its positions' windows (per frame); the tiles of all heads are list-scheduled,
 // longest first, on kNumCu * kSlotsPerCu workgroup slots. Ties go to the fewer steps.
 // Results are kept per geometry (the search takes milliseconds).
+// 32-key chunks of the window union of every position tile (tile_r x tile_c, row-major).
+std::vector<int> tile_union_chunks(int fh, int fw, int gh, int gw, bool cells, int tile_r, int tile_c) {
+  auto lo = [&](int pos, int g, int ext) { return cells ? cell_origin(pos, g) : win_origin(pos, g, ext); };
+  auto hi = [&](int pos, int g, int ext) {
+    return lo(pos, g, ext) + (cells ? cell_extent(pos, g, ext) : std::min(g, ext));
+  };
+  std::vector<int> chunks;
+  for (int r0 = 0; r0 < fh; r0 += tile_r)
+    for (int c0 = 0; c0 < fw; c0 += tile_c) {
+      const int r1 = std::min(r0 + tile_r, fh) - 1, c1 = std::min(c0 + tile_c, fw) - 1;
+      const int ur = hi(r1, gh, fh) - lo(r0, gh, fh), uc = hi(c1, gw, fw) - lo(c0, gw, fw);
+      chunks.push_back(ceil_div((int64_t)ur * uc, kStep));
+    }
+  return chunks;
+}
+
 void choose_spatial_tile(int fh, int fw, int gh, int gw, bool cells, int n_heads, int* tile_r, int* tile_c) {
   static std::mutex mu;
   static std::map<std::array<int, 6>, std::pair<int, int>> memo;
@@ -334,26 +353,15 @@ void choose_spatial_tile(int fh, int fw, int gh, int gw, bool cells, int n_heads
       return;
     }
   }
-  auto lo = [&](int pos, int g, int ext) { return cells ? cell_origin(pos, g) : win_origin(pos, g, ext); };
-  auto hi = [&](int pos, int g, int ext) {
-    return lo(pos, g, ext) + (cells ? cell_extent(pos, g, ext) : std::min(g, ext));
-  };
   double best_t = -1.0;
   int64_t best_total = 0;
   *tile_r = 4;
   *tile_c = 8;
-  std::vector<int> steps;
   for (int a = 1; a <= kSpTileMax; ++a)
     for (int b = 1; a * b <= kSpTileMax; ++b) {
       if (4 * a * b < 3 * kSpTileMax) continue;   // keep >= 3/4 of the MFMA rows busy
       if (a > fh || b > fw) continue;             // (no candidate: a frame under 24 positions keeps 4 x 8)
-      steps.clear();
-      for (int r0 = 0; r0 < fh; r0 += a)
-        for (int c0 = 0; c0 < fw; c0 += b) {
-          const int r1 = std::min(r0 + a, fh) - 1, c1 = std::min(c0 + b, fw) - 1;
-          const int ur = hi(r1, gh, fh) - lo(r0, gh, fh), uc = hi(c1, gw, fw) - lo(c0, gw, fw);
-          steps.push_back(ceil_div((int64_t)ur * uc, 32));
-        }
+      std::vector<int> steps = tile_union_chunks(fh, fw, gh, gw, cells, a, b);
       std::sort(steps.begin(), steps.end(), std::greater<int>());
       std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> slots;
       for (int i = 0; i < kNumCu * kSlotsPerCu; ++i) slots.push(0);
@@ -450,7 +458,11 @@ void plan_xcd_queues(DenseParams& p, std::vector<ItemGroup> gs) {
 }
 
 // Launch parameters of dense entries (batched by kMaxEntries), longest items first.
-hc_status dense_launches(std::vector<Entry> es, const DenseParams& base, std::vector<DenseParams>* out) {
+// With base.sp.n_sp > 0 the Spatial tiles of heads sp_heads (in the order of their
+// SpatialEntry list) follow the dense items of the single launch, each costing sp_cost
+// key tiles in the XCD queues.
+hc_status dense_launches(std::vector<Entry> es, const DenseParams& base, std::vector<DenseParams>* out,
+                         const std::vector<int>& sp_heads = {}, double sp_cost = 0.0) {
   std::stable_sort(es.begin(), es.end(), [](const Entry& a, const Entry& b) { return a.split_len > b.split_len; });
   // every item must own at least one key: the kernel's step pipeline runs n >= 1 steps
   for (const Entry& e : es)
@@ -484,6 +496,21 @@ hc_status dense_launches(std::vector<Entry> es, const DenseParams& base, std::ve
       items += e.nsplit * base.nqt;
     }
     p.n_entries = (int)n;
+    if (base.sp.n_sp > 0) {
+      if (es.size() > (size_t)kMaxEntries || (int)sp_heads.size() != base.sp.n_sp)
+        return fail(HC_ERR_STATE, "internal: Spatial tiles need one dense launch");
+      const int n_tiles = base.sp.g.tiles_r * base.sp.g.tiles_c * base.sp.g.n_parts;   // items per head
+      p.sp.n_dense_items = items;
+      for (int j = 0; j < base.sp.n_sp; ++j) {
+        int ei = -1;
+        for (size_t i = 0; i < n; ++i)
+          if (p.e[i].head == sp_heads[j]) ei = (int)i;
+        if (ei < 0) return fail(HC_ERR_STATE, "internal: Spatial head %d has no dense entry", sp_heads[j]);
+        p.sp.sp_entry[j] = (int8_t)ei;
+        groups.push_back(ItemGroup{items, n_tiles, sp_cost});
+        items += n_tiles;
+      }
+    }
     p.n_items = items;
     plan_xcd_queues(p, groups);
     out->push_back(p);
@@ -491,10 +518,11 @@ hc_status dense_launches(std::vector<Entry> es, const DenseParams& base, std::ve
   return HC_OK;
 }
 
-// Launch dense entries.
-hc_status run_dense(const std::vector<Entry>& es, const DenseParams& base, int head_dim, int bf16, hipStream_t s) {
+// Launch dense entries (and, with base.sp.n_sp > 0, the Spatial tiles after them).
+hc_status run_dense(const std::vector<Entry>& es, const DenseParams& base, int head_dim, int bf16, hipStream_t s,
+                    const std::vector<int>& sp_heads = {}, double sp_cost = 0.0) {
   std::vector<DenseParams> ps;
-  HC_TRY(dense_launches(es, base, &ps));
+  HC_TRY(dense_launches(es, base, &ps, sp_heads, sp_cost));
   for (const DenseParams& p : ps)
     HC_HIP(timed(bf16 ? K_DENSE : K_F32, s, [&] { return launch_dense(p, head_dim, bf16, s); }));
   return HC_OK;
@@ -512,6 +540,8 @@ struct Plan {
   std::vector<MergeEntry> merges;
   std::vector<SpatialEntry> spatials;
   int sp_parts = 1;                  // Spatial workgroups per tile (frame parts)
+  bool fused = false;                // Spatial tiles run as the last items of the dense launch
+                                     // (decided per fill state)
   int n_slots = 0;
   int max_slots = -1;                // partial slots the workspace provides
   int slot_cap = -1;                 // >= 0: at most this many (the library's scratch)
@@ -604,36 +634,46 @@ void build_plan(hc_head_buffers* b, Plan& P) {
   for (int h = 0; h < d.num_heads; ++h) n_sp += b->labels[h] == HC_SPATIAL;
   if (n_sp > 0 && b->sp_tile_r == 0)
     choose_spatial_tile(d.frame_h, d.frame_w, d.grid_h, d.grid_w, cells, n_sp, &b->sp_tile_r, &b->sp_tile_c);
+  // Spatial tiles run as the last items of the dense launch (bf16, d = 128, sliding
+  // windows: cells walk the current block themselves), unless the caller asks for their
+  // own launch: there they fill the slots the dense items leave idle at the end, which
+  // outweighs the merge of one more partial per Spatial head (480P-shaped layer 4.5%
+  // faster, 720P and 1080P 0.3%)
+  const bool fusable = d.dtype == HC_BF16 && d.head_dim == 128 && !cells && n_sp > 0 && n_sp <= kMaxFusedSp &&
+                       d.num_heads <= kMaxEntries && !(d.variant & HC_VARIANT_SPATIAL_OWN_LAUNCH);
+  // frame parts of their own launch: while the tiles leave workgroup slots free
   auto parts_at = [&](int64_t next_block) {
     const int n_all = (int)stored_frames(d, HC_SPATIAL, next_block) + (cells ? d.chunk_frames : 0);
     return n_sp > 0 ? spatial_parts(d, b->sp_tile_r, b->sp_tile_c, n_sp, n_all) : 1;
   };
   // partial slots of the Spatial heads: the current-block part (sliding windows) and,
-  // with frames in parts, one per part
-  auto spatial_slots = [&](int parts) {
-    return cells ? (parts > 1 ? n_sp * parts : 0) : n_sp * (parts > 1 ? 1 + parts : 1);
+  // with frames in parts or with the tiles in the dense launch, one per part
+  auto spatial_slots = [&](bool fused, int parts) {
+    return cells ? (parts > 1 ? n_sp * parts : 0) : n_sp * (fused || parts > 1 ? 1 + parts : 1);
   };
-  // The workspace is sized once, for the full window; every other fill state (more
-  // parts never, but possibly more key splits) plans within the same slots.
-  // A capped plan (the allocation-free call) takes at most slot_cap slots: fewer key
-  // splits, and no frame parts when those do not fit.
+  // The workspace is sized once, for the full window in the launch form used there;
+  // every other fill state (more parts never, but possibly more key splits; the own
+  // launch, with one slot per Spatial head, before any history frame) plans within the
+  // same slots. A capped plan (the allocation-free call) takes at most slot_cap slots:
+  // fewer key splits, and no frame parts (or the own launch) when those do not fit.
   if (P.max_slots < 0) {
     const int64_t full_block = 1 + rolling_blocks(d);
     int split_slots = 0;
     for (const Entry& e : make(full_block, -1))
       if (e.nsplit > 1) split_slots += e.nsplit;
-    P.max_slots = spatial_slots(parts_at(full_block)) + split_slots;
+    P.max_slots = (fusable ? spatial_slots(true, 1) : spatial_slots(false, parts_at(full_block))) + split_slots;
     if (P.slot_cap >= 0) P.max_slots = std::min(P.max_slots, P.slot_cap);
   }
-  P.sp_parts = parts_at(b->next_block);
-  if (spatial_slots(P.sp_parts) > P.max_slots) P.sp_parts = 1;
-  P.ok = spatial_slots(P.sp_parts) <= P.max_slots;
+  P.fused = fusable && spatial_slots(true, 1) <= P.max_slots && stored_frames(d, HC_SPATIAL, b->next_block) > 0;
+  P.sp_parts = P.fused ? 1 : parts_at(b->next_block);
+  if (spatial_slots(P.fused, P.sp_parts) > P.max_slots) P.sp_parts = 1;
+  P.ok = spatial_slots(P.fused, P.sp_parts) <= P.max_slots;
   if (!P.ok) {
     P.plan_block = -1;   // planned again (and refused again) at the next call
     return;
   }
   const int NP = P.sp_parts;
-  std::vector<Entry> es = make(b->next_block, P.max_slots - spatial_slots(NP));
+  std::vector<Entry> es = make(b->next_block, P.max_slots - spatial_slots(P.fused, NP));
   // slots: split heads and Spatial heads write fp32 partials; a Spatial head with its
   // frames in parts takes the current-block slot and one per part, merged afterwards
   int slot = 0;
@@ -663,7 +703,7 @@ void build_plan(hc_head_buffers* b, Plan& P) {
       se.head = e.head;
       se.cur_slot = e.slot;
       se.out_slot = -1;
-      if (NP > 1) {
+      if (NP > 1 || P.fused) {   // partials of the history part, merged afterwards
         se.cur_slot = -1;
         se.out_slot = slot;
         P.merges.push_back(MergeEntry{e.head, e.slot, 1 + NP, 0});
@@ -922,6 +962,52 @@ hc_status check_routed_args(const hc_head_buffers* b, const void* q, const void*
 
 // The launches of one routed call under plan P, its partial results in `workspace`
 // (at least partial_bytes(P.n_slots, ...)).
+// The Spatial launch geometry of a routed call (pointers and strides as in the dense
+// parameters p).
+void spatial_geom(const hc_head_buffers* b, const Plan& P, const DenseParams& p, SpatialGeom& g) {
+  const hc_layer_desc& d = b->desc;
+  g.q = p.q;
+  g.k_hist = p.k_hist;
+  g.v_hist = p.v_hist;
+  g.out = p.out;
+  g.part_o = p.part_o;
+  g.part_ml = p.part_ml;
+  g.hist_stride = p.hist_stride;
+  g.tok_stride = p.tok_stride;
+  g.lq = p.lq;
+  g.frame_h = d.frame_h;
+  g.frame_w = d.frame_w;
+  g.chunk_frames = d.chunk_frames;
+  g.n_hist_frames = (int)stored_frames(d, HC_SPATIAL, b->next_block);
+  g.grid_h = d.grid_h;
+  g.grid_w = d.grid_w;
+  g.tile_r = b->sp_tile_r;
+  g.tile_c = b->sp_tile_c;
+  g.tiles_r = ceil_div(d.frame_h, g.tile_r);
+  g.tiles_c = ceil_div(d.frame_w, g.tile_c);
+  g.n_parts = P.sp_parts;
+  g.scale_log2 = p.scale_log2;
+  g.cells = spatial_cells(d) ? 1 : 0;
+  g.k_cur = p.k_cur;
+  g.v_cur = p.v_cur;
+  g.n_entries = (int)P.spatials.size();
+}
+
+// With the Spatial tiles in the dense launch: their geometry in p.sp, the Spatial heads
+// in SpatialEntry order, and one item's (frame part of a tile) cost in key tiles for the
+// XCD queues (a step of 96 queries of a tile takes about 1.2 dense 128-query steps).
+void fused_spatial(const hc_head_buffers* b, const Plan& P, DenseParams& p, std::vector<int>& heads, double& cost) {
+  heads.clear();
+  cost = 0.0;
+  p.sp.n_sp = 0;
+  if (!P.fused || P.spatials.empty()) return;
+  spatial_geom(b, P, p, p.sp.g);
+  p.sp.n_sp = (int)P.spatials.size();
+  for (const SpatialEntry& se : P.spatials) heads.push_back(se.head);
+  const int frames = ceil_div(p.sp.g.n_hist_frames, p.sp.g.n_parts);
+  cost = 1.2 * spatial_max_chunks(p.sp.g) * frames * kStep / (double)kKeyTile + kItemOverheadTiles;
+}
+
 hc_status launch_routed(const hc_head_buffers* b, const Plan& P, const void* q, const void* k_cur,
                         const void* v_cur, void* out, void* workspace, hipStream_t s) {
   const hc_layer_desc& d = b->desc;
@@ -944,35 +1030,14 @@ hc_status launch_routed(const hc_head_buffers* b, const Plan& P, const void* q, 
   p.lq = (int)lq;
   p.nqt = ceil_div(lq, kDenseQ);
   p.scale_log2 = d.softmax_scale * 1.4426950408889634f;
-  HC_TRY(run_dense(P.entries, p, d.head_dim, bf16, s));
+  std::vector<int> sp_heads;
+  double sp_cost = 0.0;
+  fused_spatial(b, P, p, sp_heads, sp_cost);
+  HC_TRY(run_dense(P.entries, p, d.head_dim, bf16, s, sp_heads, sp_cost));
 
-  if (!P.spatials.empty()) {
+  if (!P.spatials.empty() && !P.fused) {
     SpatialParams sp{};
-    sp.q = q;
-    sp.k_hist = b->mem;
-    sp.v_hist = b->mem + b->v_region;
-    sp.out = out;
-    sp.part_o = part_o;
-    sp.part_ml = part_ml;
-    sp.hist_stride = d.head_dim;
-    sp.tok_stride = p.tok_stride;
-    sp.lq = (int)lq;
-    sp.frame_h = d.frame_h;
-    sp.frame_w = d.frame_w;
-    sp.chunk_frames = d.chunk_frames;
-    sp.n_hist_frames = (int)stored_frames(d, HC_SPATIAL, b->next_block);
-    sp.grid_h = d.grid_h;
-    sp.grid_w = d.grid_w;
-    sp.tile_r = b->sp_tile_r;
-    sp.tile_c = b->sp_tile_c;
-    sp.tiles_r = ceil_div(d.frame_h, sp.tile_r);
-    sp.tiles_c = ceil_div(d.frame_w, sp.tile_c);
-    sp.n_parts = P.sp_parts;
-    sp.scale_log2 = p.scale_log2;
-    sp.cells = spatial_cells(d) ? 1 : 0;
-    sp.k_cur = k_cur;
-    sp.v_cur = v_cur;
-    sp.n_entries = (int)P.spatials.size();
+    spatial_geom(b, P, p, sp);
     for (size_t i = 0; i < P.spatials.size(); ++i) sp.e[i] = P.spatials[i];
     HC_HIP(timed(bf16 ? K_SPATIAL : K_F32, s, [&] { return launch_spatial(sp, d.head_dim, bf16, s); }));
   }
@@ -1339,8 +1404,11 @@ hc_status hc_debug_dense_queues(const hc_head_buffers* b, int32_t* runs, int32_t
   DenseParams base{};
   base.lq = (int)lq_of(b->desc);
   base.nqt = ceil_div(base.lq, kDenseQ);
+  std::vector<int> sp_heads;
+  double sp_cost = 0.0;
+  fused_spatial(b, b->plan, base, sp_heads, sp_cost);
   std::vector<DenseParams> ps;
-  HC_TRY(dense_launches(b->plan.entries, base, &ps));
+  HC_TRY(dense_launches(b->plan.entries, base, &ps, sp_heads, sp_cost));
   for (int x = 0; x < kXcds; ++x) n_runs[x] = 0;
   *queue_len = 0;
   if (ps.empty()) return ok();
@@ -1363,6 +1431,7 @@ hc_status hc_debug_spatial_plan(const hc_head_buffers* b, int32_t* plan) {
   plan[1] = any ? b->sp_tile_c : 0;
   plan[2] = any ? b->plan.sp_parts : 0;
   plan[3] = b->plan.n_slots;
+  plan[4] = any && b->plan.fused ? 1 : 0;
   return ok();
 }
 

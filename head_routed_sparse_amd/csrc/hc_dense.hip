@@ -15,35 +15,38 @@
 // which the softmax needs more, with half the matrix work per score. The step pipeline
 // (direct loads into an LDS ring, transposed V reads, reference-max softmax) is in
 // hc_pipe.h.
-#include "hc_pipe.h"
+//
+// For d = 128 with Spatial heads on sliding windows, the routed call appends the
+// Spatial path's tiles (hc_spatial_tile.h) to the launch as its last, shortest items:
+// they fill the workgroup slots that the dense items leave idle at the end, and write
+// fp32 partials that the merge kernel joins with the heads' current-block partials.
+#include "hc_spatial_tile.h"
 
 namespace hc {
 
 namespace {
 
+// This workgroup's item: position blockIdx.x / 8 of the queue of XCD blockIdx.x % 8
+// (-1 past the end of the queue).
+__device__ __forceinline__ int queue_item(const DenseParams& p) {
+  const int xq = blockIdx.x % kXcds;
+  int k = blockIdx.x / kXcds;
+  for (int r = 0; r < p.xcd_nrun[xq]; ++r) {
+    if (k < p.xcd_run[xq][r].count) return p.xcd_run[xq][r].first + k;
+    k -= p.xcd_run[xq][r].count;
+  }
+  return -1;
+}
+
+// One dense item (128 queries of one head against one key split) with the LDS ring at
+// `lds` (four stages).
 template <int D, int QB>
-__global__ __launch_bounds__(64 * (kDenseQ / (32 * QB)), kDenseQ / (32 * QB) >= 8 ? 1 : 8 / (kDenseQ / (32 * QB)))
-void dense_attn_bf16(const DenseParams p) {
+__device__ __forceinline__ void dense_item(const DenseParams& p, int item, lds_char* lds) {
   constexpr int W = kDenseQ / (32 * QB);   // waves per workgroup
   using R = Ring<D, QB, W>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int NS = 4;   // ring stages
-  __shared__ __attribute__((aligned(1024))) char ring[NS * R::kStageBytes];
-  lds_char* const lds = (lds_char*)ring;
-
-  // this workgroup's item: position blockIdx.x / 8 of the queue of XCD blockIdx.x % 8
-  const int xq = blockIdx.x % kXcds;
-  int k = blockIdx.x / kXcds;
-  int item = -1;
-  for (int r = 0; r < p.xcd_nrun[xq]; ++r) {
-    if (k < p.xcd_run[xq][r].count) {
-      item = p.xcd_run[xq][r].first + k;
-      break;
-    }
-    k -= p.xcd_run[xq][r].count;
-  }
-  if (item < 0) return;
   int ei = 0;
   while (ei + 1 < p.n_entries && item >= p.e[ei + 1].item_begin) ++ei;
   const DenseEntry e = p.e[ei];
@@ -159,6 +162,42 @@ void dense_attn_bf16(const DenseParams p) {
   }
 }
 
+template <int D, int QB>
+__global__ __launch_bounds__(64 * (kDenseQ / (32 * QB)), kDenseQ / (32 * QB) >= 8 ? 1 : 8 / (kDenseQ / (32 * QB)))
+void dense_attn_bf16(const DenseParams p) {
+  constexpr int W = kDenseQ / (32 * QB);
+  __shared__ __attribute__((aligned(1024))) char ring[4 * Ring<D, QB, W>::kStageBytes];
+  const int item = queue_item(p);
+  if (item < 0) return;
+  dense_item<D, QB>(p, item, (lds_char*)ring);
+}
+
+// Dense items, then the Spatial tiles (d = 128). Both use four waves and a four-stage
+// ring of the same layout; the LDS adds the Spatial tables when TABLE.
+template <bool TABLE>
+__global__ __launch_bounds__(256, 2) void dense_spatial_bf16(const DenseParams p) {
+  static_assert(4 * Ring<128, 1, 4>::kStageBytes <= spatial_lds_bytes<128, TABLE>(), "shared ring");
+  __shared__ __attribute__((aligned(1024))) char ring[spatial_lds_bytes<128, TABLE>()];
+  const int item = queue_item(p);
+  if (item < 0) return;
+  if (item < p.sp.n_dense_items) {
+    dense_item<128, 1>(p, item, (lds_char*)ring);
+    return;
+  }
+  // item s of the Spatial items: tile s % n_tiles, frame part s / n_tiles % n_parts of
+  // the head s / (n_tiles * n_parts)
+  const int n_tiles = p.sp.g.tiles_r * p.sp.g.tiles_c;
+  const int s = item - p.sp.n_dense_items;
+  const DenseEntry d = p.e[p.sp.sp_entry[s / (n_tiles * p.sp.g.n_parts)]];
+  SpatialEntry e;
+  e.hist_off = d.hist_off;
+  e.head = d.head;
+  e.cur_slot = -1;
+  e.out_slot = d.slot + 1;
+  e.pad = 0;
+  spatial_tile<128, TABLE>(p.sp.g, e, s % n_tiles, s / n_tiles % p.sp.g.n_parts, (lds_char*)ring);
+}
+
 }  // namespace
 
 hipError_t launch_dense_f32(const DenseParams& p, int head_dim, hipStream_t s);
@@ -168,7 +207,13 @@ hipError_t launch_dense(const DenseParams& p, int head_dim, int bf16, hipStream_
   if (!bf16) return launch_dense_f32(p, head_dim, s);
   // four waves of 32 queries for both head sizes
   const dim3 grid(kXcds * p.xcd_len);
-  if (head_dim == 64)
+  if (p.sp.n_sp > 0) {   // with the Spatial tiles (d = 128 only)
+    if (head_dim != 128) return hipErrorInvalidValue;
+    if (spatial_table(p.sp.g))
+      hipLaunchKernelGGL((dense_spatial_bf16<true>), grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((dense_spatial_bf16<false>), grid, dim3(256), 0, s, p);
+  } else if (head_dim == 64)
     hipLaunchKernelGGL((dense_attn_bf16<64, 1>), grid, dim3(64 * (kDenseQ / 32)), 0, s, p);
   else
     hipLaunchKernelGGL((dense_attn_bf16<128, 1>), grid, dim3(64 * (kDenseQ / 32)), 0, s, p);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace hc {
 
 constexpr int kMaxEntries = 64;   // dense work entries per launch (kernel arguments by value)
@@ -12,6 +14,7 @@ constexpr int kDenseQ = 128;      // queries per dense workgroup (query tile)
 constexpr int kXcds = 8;          // XCDs; workgroup i is dispatched to XCD i % 8, in order i / 8
 constexpr int kXcdRuns = 16;      // runs of consecutive items in one XCD's queue
 constexpr int kSpTileMax = 32;    // positions per Spatial query tile (one 32-query MFMA block)
+constexpr int kStep = 32;         // keys per pipeline step
 
 // First row (or column) of the g-wide Spatial window around pos in a frame of `extent`
 // rows (columns): the query sits at offset g/2, and the window is shifted (never cut)
@@ -51,48 +54,6 @@ struct XcdRun {
   int32_t count;
 };
 
-struct DenseParams {
-  const void* q;         // [lq][H][D]
-  const void* k_hist;    // history rows, row stride hist_stride elements
-  const void* v_hist;
-  const void* k_cur;     // [C*S][H][D]
-  const void* v_cur;
-  void* out;             // [lq][H][D], same dtype as q
-  float* part_o;         // [slot][lq][D] fp32, unnormalised
-  float* part_ml;        // [slot][lq][2]: running max (log2 units, scale folded) and sum
-  int64_t hist_stride;   // elements between consecutive history rows
-  int64_t tok_stride;    // H*D: elements between tokens of q / k_cur / v_cur / out
-  int32_t lq;            // queries per head
-  int32_t nqt;           // query tiles per head
-  int32_t n_entries;
-  int32_t n_items;
-  float scale_log2;      // softmax_scale * log2(e)
-  int32_t xcd_len;       // workgroups of each XCD's queue (grid = kXcds * xcd_len)
-  DenseEntry e[kMaxEntries];
-  int32_t xcd_nrun[kXcds];           // runs in each XCD's queue
-  XcdRun xcd_run[kXcds][kXcdRuns];   // queue x = the items of its runs, in order
-};
-
-// Merge of partial slots into the normalised output (split keys, Spatial merge).
-struct MergeEntry {
-  int32_t head;
-  int32_t slot;
-  int32_t nslot;
-  int32_t pad;
-};
-
-struct MergeParams {
-  const float* part_o;
-  const float* part_ml;
-  void* out;
-  int64_t tok_stride;
-  int32_t lq;
-  int32_t n_entries;
-  int32_t head_dim;
-  int32_t pad;
-  MergeEntry e[kMaxEntries];
-};
-
 // Spatial history gather for the Spatial heads: every query (f, r, c) of the current
 // block against the g x g window of every history frame; merged with the dense
 // current-block partial held in cur_slot (final mode), or written as a partial.
@@ -104,7 +65,7 @@ struct SpatialEntry {
   int32_t pad;
 };
 
-struct SpatialParams {
+struct SpatialGeom {
   const void* q;
   const void* k_hist;
   const void* v_hist;
@@ -127,8 +88,97 @@ struct SpatialParams {
                            //    block read from k_cur / v_cur), output written directly
   const void* k_cur;       // [C*S][H][D], cell mode only
   const void* v_cur;
+};
+
+struct SpatialParams : SpatialGeom {
   SpatialEntry e[kMaxEntries];
 };
+
+// Spatial tiles as the last items of a dense launch (d = 128, bf16, sliding windows):
+// item n_dense_items + s is tile s % tiles, frame part s / tiles % g.n_parts, of Spatial
+// head entry e[sp_entry[s / (tiles * g.n_parts)]]; part i writes the partial of slot
+// e[...].slot + 1 + i, which the merge kernel joins with the current-block partial in
+// e[...].slot.
+constexpr int kMaxFusedSp = 16;
+struct FusedSpatial {
+  SpatialGeom g;           // q, out, partials and strides as in the dense parameters
+  int32_t n_dense_items;   // items below are dense items
+  int32_t n_sp;            // Spatial head entries (0: no Spatial items)
+  int8_t sp_entry[kMaxFusedSp];
+};
+
+// Unions of up to this many 32-key chunks keep their per-chunk tables in LDS.
+constexpr int kTblChunks = 8;
+
+// 32-key chunks of the largest union of a tile's windows; rows and columns of the union
+// vary independently, so the largest union is the product of the largest row and
+// column extents. Host code.
+inline int spatial_max_chunks(const SpatialGeom& p) {
+  int ur = 0, uc = 0;
+  const bool cells = p.cells != 0;
+  for (int r0 = 0; r0 < p.frame_h; r0 += p.tile_r) {
+    const int r1 = std::min(r0 + p.tile_r, p.frame_h) - 1;
+    const int lo = cells ? cell_origin(r0, p.grid_h) : win_origin(r0, p.grid_h, p.frame_h);
+    const int hi = cells ? cell_origin(r1, p.grid_h) + cell_extent(r1, p.grid_h, p.frame_h)
+                         : win_origin(r1, p.grid_h, p.frame_h) + std::min(p.grid_h, p.frame_h);
+    ur = std::max(ur, hi - lo);
+  }
+  for (int c0 = 0; c0 < p.frame_w; c0 += p.tile_c) {
+    const int c1 = std::min(c0 + p.tile_c, p.frame_w) - 1;
+    const int lo = cells ? cell_origin(c0, p.grid_w) : win_origin(c0, p.grid_w, p.frame_w);
+    const int hi = cells ? cell_origin(c1, p.grid_w) + cell_extent(c1, p.grid_w, p.frame_w)
+                         : win_origin(c1, p.grid_w, p.frame_w) + std::min(p.grid_w, p.frame_w);
+    uc = std::max(uc, hi - lo);
+  }
+  return (ur * uc + kStep - 1) / kStep;
+}
+
+// Whether every tile's union fits the tables (kTblChunks chunks). Host code.
+inline bool spatial_table(const SpatialGeom& p) { return spatial_max_chunks(p) <= kTblChunks; }
+
+struct DenseParams {
+  const void* q;         // [lq][H][D]
+  const void* k_hist;    // history rows, row stride hist_stride elements
+  const void* v_hist;
+  const void* k_cur;     // [C*S][H][D]
+  const void* v_cur;
+  void* out;             // [lq][H][D], same dtype as q
+  float* part_o;         // [slot][lq][D] fp32, unnormalised
+  float* part_ml;        // [slot][lq][2]: running max (log2 units, scale folded) and sum
+  int64_t hist_stride;   // elements between consecutive history rows
+  int64_t tok_stride;    // H*D: elements between tokens of q / k_cur / v_cur / out
+  int32_t lq;            // queries per head
+  int32_t nqt;           // query tiles per head
+  int32_t n_entries;
+  int32_t n_items;
+  float scale_log2;      // softmax_scale * log2(e)
+  int32_t xcd_len;       // workgroups of each XCD's queue (grid = kXcds * xcd_len)
+  DenseEntry e[kMaxEntries];
+  int32_t xcd_nrun[kXcds];           // runs in each XCD's queue
+  XcdRun xcd_run[kXcds][kXcdRuns];   // queue x = the items of its runs, in order
+  FusedSpatial sp;                   // n_sp > 0: Spatial tiles after the dense items
+};
+
+// Merge of partial slots into the normalised output (split keys, Spatial merge).
+struct MergeEntry {
+  int32_t head;
+  int32_t slot;
+  int32_t nslot;
+  int32_t pad;
+};
+
+struct MergeParams {
+  const float* part_o;
+  const float* part_ml;
+  void* out;
+  int64_t tok_stride;
+  int32_t lq;
+  int32_t n_entries;
+  int32_t head_dim;
+  int32_t pad;
+  MergeEntry e[kMaxEntries];
+};
+
 
 // Row copy: `rows` rows of row_bytes from src (byte offset src_off, byte stride
 // src_stride) to contiguous rows at dst byte offset dst_off. K and V move together.

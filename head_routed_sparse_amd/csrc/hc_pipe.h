@@ -14,7 +14,6 @@
 
 namespace hc {
 
-constexpr int kStep = 32;     // keys per pipeline step
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;

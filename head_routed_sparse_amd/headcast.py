@@ -29,7 +29,7 @@ LIB_PATH = os.environ.get("HEADCAST_LIBRARY") or os.path.join(HERE, "libheadcast
 
 SINK, DUMMY, SPATIAL, GLOBAL = 0, 1, 2, 3
 HC_BF16, HC_F32 = 0, 1
-HC_VARIANT_DUMMY_PREVIOUS, HC_VARIANT_SPATIAL_CELLS = 1, 2
+HC_VARIANT_DUMMY_PREVIOUS, HC_VARIANT_SPATIAL_CELLS, HC_VARIANT_SPATIAL_OWN_LAUNCH = 1, 2, 4
 KERNEL_KINDS = ("dense", "merge", "spatial", "copy", "stats", "fp32")
 
 
@@ -381,8 +381,9 @@ def hc_debug_dense_queues(buffers: HeadBuffers):
 
 
 def hc_debug_spatial_plan(buffers: HeadBuffers):
-    """(tile rows, tile columns, frame parts, partial slots) of the routed call."""
-    p = np.zeros(4, np.int32)
+    """(tile rows, tile columns, frame parts, partial slots, Spatial tiles in the dense
+    launch) of the routed call."""
+    p = np.zeros(5, np.int32)
     _check(lib().hc_debug_spatial_plan(buffers.handle, p.ctypes.data_as(_P)))
     return tuple(int(x) for x in p)
 

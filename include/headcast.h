@@ -65,8 +65,19 @@ typedef enum { HC_BF16 = 0, HC_F32 = 1 } hc_dtype;
  *  HC_VARIANT_SPATIAL_CELLS: Spatial heads attend only the keys of their own
  *    non-overlapping grid_h x grid_w cell (cells tile the frame from (0,0); the last
  *    row/column of cells keeps the remainder) in every window frame, the current block
- *    included (Sec. 4.4, Fig. 3; Sec. 5.1 uses 10 x 10 cells). */
-typedef enum { HC_VARIANT_DUMMY_PREVIOUS = 1, HC_VARIANT_SPATIAL_CELLS = 2 } hc_variant;
+ *    included (Sec. 4.4, Fig. 3; Sec. 5.1 uses 10 x 10 cells).
+ * A launch option (results equal up to rounding order, within the bf16 tolerance):
+ *  HC_VARIANT_SPATIAL_OWN_LAUNCH: the Spatial heads' history part runs as its own
+ *    kernel after the dense launch. Without it, for bf16 with head_dim 128, sliding
+ *    windows and at most 16 Spatial heads, the routed call runs the Spatial tiles as the
+ *    last items of the dense launch, where they fill the workgroup slots the dense
+ *    items leave idle at the end, and merges their partials afterwards (one more
+ *    partial slot per Spatial head in the workspace). */
+typedef enum {
+  HC_VARIANT_DUMMY_PREVIOUS = 1,
+  HC_VARIANT_SPATIAL_CELLS = 2,
+  HC_VARIANT_SPATIAL_OWN_LAUNCH = 4
+} hc_variant;
 
 typedef struct {
   int32_t num_heads;      /* H, 1..64 */
@@ -224,9 +235,13 @@ int32_t hc_decide(double cos_sink, double cos_dummy, double cos_spatial, double 
  * hc_debug_dense_queues: the XCD queues of the routed call's (first) dense launch: host
  * runs [8][16][2] = {first item, items} (-1 / 0 past n_runs[x]), n_runs [8], and the
  * longest queue; workgroup i runs on XCD i % 8, taking position i / 8 of its queue.
- * hc_debug_spatial_plan: the Spatial launch of a routed call, host [4] = {tile rows,
- * tile columns, frame parts, partial slots of the whole call}; zeros without Spatial
- * heads. Pure host. */
+ * With the Spatial tiles in the launch, items from the dense item count on (see
+ * hc_debug_routed_plan) are the tiles, Spatial head by head in head order within the
+ * SpatialEntry list, tile_r x tile_c position tiles each.
+ * hc_debug_spatial_plan: the Spatial launch of a routed call, host [5] = {tile rows,
+ * tile columns, frame parts, partial slots of the whole call, 1 if the Spatial tiles
+ * run as the last items of the dense launch}; zeros without Spatial heads (the slot
+ * count excepted). Pure host. */
 hc_status hc_debug_slot_table(const hc_head_buffers* buffers, int32_t* frames);
 hc_status hc_debug_head_region(const hc_head_buffers* buffers, int32_t head, int64_t* k_offset,
                                int64_t* v_offset, int64_t* rows);

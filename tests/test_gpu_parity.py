@@ -81,21 +81,22 @@ def test_spatial_grids(grid):
 
 
 @pytest.mark.parametrize("frame", [(3, 40), (40, 3), (2, 2), (1, 50), (7, 7), (5, 6)])
-@pytest.mark.parametrize("variant", [0, 2])
+@pytest.mark.parametrize("variant", [0, 2, 4])
 def test_spatial_tiles_on_odd_frames(frame, variant):
     """Frames narrower or shorter than any 24..32-position tile, or smaller than 24
-    positions (the 4 x 8 fallback tile), with several frame parts and, for the cell
-    variant, cells cut at the frame edge."""
+    positions (the 4 x 8 fallback tile): the tiles in the dense launch (variant 0), in
+    their own launch with several frame parts (variant 4), and for the cell variant,
+    cells cut at the frame edge."""
     fh, fw = frame
     g = hin.Geometry(4, 128, fh, fw, 3, 12, 3, 4, "bf16")
     inp = hin.generate(g, (P_, G_, P_, S_), seed=fh * 100 + fw + variant)
     t = to_device(inp)
     buf = hc.hc_build_head_buffers(hc.make_desc(g, variant), inp.labels, t["k_hist"], t["v_hist"],
                                    inp.n_hist_frames)
-    tile_r, tile_c, parts, _ = hc.hc_debug_spatial_plan(buf)
-    assert tile_r * tile_c <= 32 and parts >= 1
+    tile_r, tile_c, parts, _, fused = hc.hc_debug_spatial_plan(buf)
+    assert tile_r * tile_c <= 32 and parts >= 1 and fused == (variant == 0)
     got = host(hc.hc_routed_attention(buf, t["q"], t["k_cur"], t["v_cur"]))
-    want = orc.routed_attention(inp, variant=variant)
+    want = orc.routed_attention(inp, variant=variant & 3)
     print(frame, variant, (tile_r, tile_c, parts),
           assert_close(got, want, *TOL["bf16"], what=f"{frame} v{variant} tile {tile_r}x{tile_c} parts {parts}"))
 
@@ -295,20 +296,22 @@ def test_rollout_routed_matches_oracle_window(dtype):
 
 @pytest.mark.parametrize("name", ["480p", "720p", "1080p"])
 def test_full_size_sampled_rows(name):
-    """The benchmark's workloads at full size; sampled query rows against the oracle,
-    plus the all-Global call of the same kernel."""
+    """The benchmark's workloads at full size; sampled query rows against the oracle, the
+    routed call in both launch forms of the Spatial path (in the dense launch, its own
+    launch), plus the all-Global call of the same kernel."""
     inp = hin.config_inputs(name)
     g = inp.geom
     t = to_device(inp)
-    d = hc.make_desc(g)
     rows = sample_rows(g, n_random=512, seed=1)
-    for labels in (inp.labels, np.full(g.num_heads, G_, np.int32)):
-        buf = hc.hc_build_head_buffers(d, labels, t["k_hist"], t["v_hist"], inp.n_hist_frames)
-        out = host(hc.hc_routed_attention(buf, t["q"], t["k_cur"], t["v_cur"]))
+    for labels, variants in ((inp.labels, (0, 4)), (np.full(g.num_heads, G_, np.int32), (0,))):
         want = orc.routed_attention(inp, labels=labels, rows=rows)
-        print(name, labels, assert_close(out[rows], want, *TOL["bf16"], what=name))
-        assert np.isfinite(out).all()
-        del buf
+        for v in variants:
+            buf = hc.hc_build_head_buffers(hc.make_desc(g, v), labels, t["k_hist"], t["v_hist"], inp.n_hist_frames)
+            out = host(hc.hc_routed_attention(buf, t["q"], t["k_cur"], t["v_cur"]))
+            print(name, labels, v, hc.hc_debug_spatial_plan(buf),
+                  assert_close(out[rows], want, *TOL["bf16"], what=f"{name} v{v}"))
+            assert np.isfinite(out).all()
+            del buf
 
 
 def test_deterministic_bitwise():

@@ -42,7 +42,7 @@ def desc_of(name="720p", **kw):
 @pytest.mark.parametrize("field,value,status", [
     ("head_dim", 96, 2), ("num_heads", 0, 2), ("num_heads", 65, 2), ("dtype", 7, 3),
     ("window_frames", 20, 2), ("chunk_frames", 0, 2), ("grid_h", 0, 2), ("frame_w", 0, 2),
-    ("softmax_scale", -1.0, 2), ("frame_w", 30000, 2)])
+    ("softmax_scale", -1.0, 2), ("frame_w", 30000, 2), ("variant", 8, 2)])
 def test_desc_validation(field, value, status):
     d = desc_of(**{field: value})
     with pytest.raises(hc.HCError) as ei:
@@ -145,17 +145,50 @@ def test_routed_plan_covers_every_key_once(name, next_block):
         assert list(ents[:, 4]) == sorted(ents[:, 4], reverse=True)
 
 
-def planned_balance(pb, g):
+def spatial_tile_chunks(g, tile_r, tile_c):
+    """32-key chunks of the window union of every position tile (row-major)."""
+    def org(p, gg, ext):
+        return min(max(p - gg // 2, 0), max(ext - gg, 0))
+
+    steps = []
+    for r0 in range(0, g.frame_h, tile_r):
+        r1 = min(r0 + tile_r, g.frame_h) - 1
+        ur = org(r1, g.grid_h, g.frame_h) + min(g.grid_h, g.frame_h) - org(r0, g.grid_h, g.frame_h)
+        for c0 in range(0, g.frame_w, tile_c):
+            c1 = min(c0 + tile_c, g.frame_w) - 1
+            uc = org(c1, g.grid_w, g.frame_w) + min(g.grid_w, g.frame_w) - org(c0, g.grid_w, g.frame_w)
+            steps.append(-(-ur * uc // 32))
+    return steps
+
+
+def spatial_item_steps(g, tile_r, tile_c, parts, n_hist):
+    """Steps of the Spatial items of one head in launch order: frame part by frame part,
+    tile by tile; part i walks frames [i n_hist / parts, (i + 1) n_hist / parts)."""
+    chunks = spatial_tile_chunks(g, tile_r, tile_c)
+    return [c * ((i + 1) * n_hist // parts - i * n_hist // parts) for i in range(parts) for c in chunks]
+
+
+def item_costs(pb, g, labels):
+    """32-key steps of every item of the dense launch: the dense items, then (when the
+    Spatial tiles run in it) the tiles of each Spatial head."""
+    ents, n_items = hc.hc_debug_routed_plan(pb)
+    nqt = -(-g.lq // int(ents[0, 7]))
+    cost = []
+    for head, hist, cur, nsplit, split_len, slot, begin, _q in ents:
+        for s in range(nsplit):
+            cost += [-(-min(split_len, hist + cur - s * split_len) // 32)] * nqt
+    tr, tc, parts, _, fused = hc.hc_debug_spatial_plan(pb)
+    if fused:
+        cost += spatial_item_steps(g, tr, tc, parts, g.hist_frames) * int(np.sum(np.asarray(labels) == 2))
+    return np.array(cost, np.int64), n_items
+
+
+def planned_balance(pb, g, labels):
     """Sum of the items' 32-key steps over 512 slots x the longest slot, each XCD's queue
     dealt in order to its 64 slots (32 CUs x 2 workgroups), each item to the slot that
     frees first."""
     import heapq
-    ents, n_items = hc.hc_debug_routed_plan(pb)
-    nqt = -(-g.lq // int(ents[0, 7]))
-    cost = np.zeros(n_items, np.int64)
-    for head, hist, cur, nsplit, split_len, slot, begin, _q in ents:
-        for s in range(nsplit):
-            cost[begin + s * nqt:begin + (s + 1) * nqt] = -(-min(split_len, hist + cur - s * split_len) // 32)
+    cost, _ = item_costs(pb, g, labels)
     queues, _ = hc.hc_debug_dense_queues(pb)
     span = 0
     for q in queues:
@@ -185,7 +218,7 @@ def test_key_splits_per_class_and_planned_balance(name, floor):
             if lab[head] != 2:   # a Spatial head's current block is never split
                 by_len.setdefault(total, set()).add((int(nsplit), int(split_len)))
         assert all(len(v) == 1 for v in by_len.values()), by_len
-        assert planned_balance(pb, g) >= floor
+        assert planned_balance(pb, g, lab) >= floor
 
 
 @pytest.mark.parametrize("name", ["tiny", "480p", "720p", "1080p"])
@@ -203,14 +236,17 @@ def test_routed_workspace_fits_every_fill_state(name, variant):
         assert len(sizes) == 1, (name, variant, lab, sizes)
 
 
-@pytest.mark.parametrize("name,variant,want", [("720p", 0, (5, 6, 1)), ("480p", 0, (5, 6, 3)),
-                                               ("1080p", 0, (4, 8, 1)), ("720p", 2, (5, 5, 1)),
-                                               ("480p", 2, (5, 5, 2))])
+@pytest.mark.parametrize("name,variant,want", [("720p", 0, (5, 6, 1, 1)), ("480p", 0, (5, 6, 1, 1)),
+                                               ("1080p", 0, (4, 8, 1, 1)), ("720p", 2, (5, 5, 1, 0)),
+                                               ("480p", 2, (5, 5, 2, 0)), ("480p", 4, (5, 6, 3, 0)),
+                                               ("720p", 4, (5, 6, 1, 0))])
 def test_spatial_plan(name, variant, want):
-    """Spatial tile and frame parts at the bench sizes: 24..32 positions inside the frame,
-    parts only while the tiles leave workgroup slots free, at most one per frame, and
-    the partial slots (current block + one per part per Spatial head, plus the key
-    splits) within the workspace."""
+    """Spatial tile, frame parts and launch form at the bench sizes: 24..32 positions
+    inside the frame; sliding windows run their tiles in the dense launch (current-block
+    and history partial per Spatial head) unless variant 4 asks for their own launch; in
+    their own launch, parts only while the tiles leave workgroup slots free, at most one
+    per frame; the partial slots (those of the Spatial heads plus the key splits) within
+    the workspace."""
     cfg = hin.CONFIGS[name]
     g = cfg["geom"]
     if variant & 2:   # the pages' 10 x 10 cells
@@ -218,14 +254,21 @@ def test_spatial_plan(name, variant, want):
     lab = cfg["labels"]
     n_sp = int((lab == 2).sum())
     pb = hc.hc_plan_head_buffers(hc.make_desc(g, variant), lab, g.window_frames // g.chunk_frames - 1)
-    tr, tc, parts, slots = hc.hc_debug_spatial_plan(pb)
-    assert (tr, tc, parts) == want
+    tr, tc, parts, slots, fused = hc.hc_debug_spatial_plan(pb)
+    assert (tr, tc, parts, fused) == want
     assert 24 <= tr * tc <= 32 and tr <= g.frame_h and tc <= g.frame_w
     tiles = -(-g.frame_h // tr) * -(-g.frame_w // tc) * n_sp
-    assert parts == max(1, min(512 // tiles, 4, g.hist_frames + (g.chunk_frames if variant & 2 else 0)))
+    if not fused:
+        assert parts == max(1, min(512 // tiles, 4, g.hist_frames + (g.chunk_frames if variant & 2 else 0)))
     ents, _ = hc.hc_debug_routed_plan(pb)
     split_slots = int(sum(e[3] for e in ents if e[3] > 1))
-    sp_slots = (n_sp * parts if parts > 1 else 0) if variant & 2 else n_sp * (1 + parts if parts > 1 else 1)
+    if fused:
+        assert parts == 1
+        sp_slots = 2 * n_sp
+    elif variant & 2:
+        sp_slots = n_sp * parts if parts > 1 else 0
+    else:
+        sp_slots = n_sp * (1 + parts if parts > 1 else 1)
     assert slots == split_slots + sp_slots
     assert hc.hc_routed_workspace_bytes(pb) >= slots * g.lq * (g.head_dim + 2) * 4
     # no Spatial heads: no Spatial launch
@@ -311,7 +354,10 @@ def test_variant_plans():
         base = hc.hc_head_buffers_bytes(hc.make_desc(g, 0), cfg["labels"])
         assert n - base == (2 * 3 * g.chunk_frames * S * g.head_dim * 2 if var & 1 else 0)
     with pytest.raises(hc.HCError):
-        hc.hc_head_buffers_bytes(hc.make_desc(g, 4), cfg["labels"])
+        hc.hc_head_buffers_bytes(hc.make_desc(g, 8), cfg["labels"])
+    # the launch option changes no buffer
+    assert hc.hc_head_buffers_bytes(hc.make_desc(g, 4), cfg["labels"]) == \
+        hc.hc_head_buffers_bytes(hc.make_desc(g, 0), cfg["labels"])
 
 
 def test_build_at_block_validates_the_window_length():
@@ -367,8 +413,17 @@ def test_dense_xcd_queues_cover_items_balanced_longest_first(name, global_only):
     for head, hist, cur, nsplit, split_len, slot, item_begin, _q in ents:
         for sp in range(nsplit):
             lo = item_begin + sp * nqt
-            cost[lo:lo + nqt] = min(split_len, hist + cur - sp * split_len) / 64 + 3.0
+            cost[lo:lo + nqt] = min(split_len, hist + cur - sp * split_len) / 64 + 9.0
             group[lo:lo + nqt] = lo
+    tr, tc, parts, _, fused = hc.hc_debug_spatial_plan(pb)
+    if fused:   # then the Spatial items, head by head, one class of the planner's item cost
+        n_sp = int(np.sum(labels == 2))
+        n_per = -(-g.frame_h // tr) * -(-g.frame_w // tc) * parts
+        n_hist = len(orc.window_history_blocks(7, g.window_frames, g.chunk_frames)) * g.chunk_frames
+        chunks = max(spatial_tile_chunks(g, tr, tc))
+        cost = np.concatenate([cost, np.full(n_sp * n_per, 1.2 * chunks * -(-n_hist // parts) * 32 / 64 + 9.0)])
+        group = np.concatenate([group, n_items + (np.arange(n_sp * n_per) // n_per) * n_per])
+        n_items += n_sp * n_per
     seen = np.zeros(n_items, np.int64)
     per_class = {}
     spans = {}
