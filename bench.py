@@ -41,6 +41,8 @@ def parse():
                     help="skip the 30-layer planted step")
     ap.add_argument("--labels", default="", choices=["", "global"],
                     help="profiling runs: 'global' times the full-window call instead of the routed one")
+    ap.add_argument("--spatial-own-launch", action="store_true",
+                    help="with --only-routed: the Spatial path as its own kernel (for profiling it)")
     ap.add_argument("--only-routed", action="store_true",
                     help="profiling runs: time only the routed call of the main workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -89,7 +91,7 @@ def spatial_mfma_flops(geom, n_sp, n_hist, tile_r, tile_c):
 
 
 KERNEL_SOURCES = ["hc_dense.hip", "hc_spatial_tile.h", "hc_pipe.h", "hc_mfma.h", "hc_internal.h"]
-COUNTERS = os.path.join(ROOT, "profiles", "dense_attn_bf16_720p_counters.json")
+COUNTERS = os.path.join(ROOT, "profiles", "dense_spatial_bf16_720p_counters.json")
 
 
 def measured_traffic(workload):
@@ -617,7 +619,8 @@ def main():
         print(f"[bench] copy calibration: {n} bytes read, {n} bytes written", file=sys.stderr, flush=True)
         del src, dst
     main_res = measure(a.config, a.steps, a.warmup, with_events=True, only_routed=a.only_routed,
-                       labels_override=a.labels)
+                       labels_override=a.labels,
+                       variant=hc.HC_VARIANT_SPATIAL_OWN_LAUNCH if a.only_routed and a.spatial_own_launch else 0)
     g = main_res["geom"]
     if a.only_routed:
         r = main_res["routed"]
