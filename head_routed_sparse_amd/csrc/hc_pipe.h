@@ -251,8 +251,11 @@ struct LaneAddr {
 //   active:          false for a wave with no queries of its own: it still issues its
 //                    share of the loads and meets every barrier, but skips the math.
 //   kEarlyV:         read the step's V^T fragments right after the barrier (their stage
-//                    stays put for the whole step) instead of just before the PV product:
-//                    32 more live registers, less exposed LDS latency per step.
+//                    stays put for the whole step); otherwise after the score MFMAs and
+//                    the softmax, before the step's loads go out, so that the reads land
+//                    while the load addresses are worked out and the PV MFMAs then issue
+//                    back to back. Early reads hold 32 more registers over the score
+//                    phase (they pay in the Spatial kernel, the later ones in the dense).
 template <int D, int QB, int W, int NS, bool kEarlyV, class Issue, class Prep, class Soft>
 __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D, QB, W>& la,
                                           const u32x4 (&q)[QB][D / 16], Block<D> (&blk)[QB], bool active,
@@ -289,26 +292,14 @@ __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D
         vf[s2][db] = u32x4{l2[0], l2[1], h2[0], h2[1]};
       }
   };
-  // O^T += V^T P^T of a step for every block (each V^T fragment used QB times), from
-  // fragments read before, or (stage >= 0) read here, each just before its products
-  auto pv = [&](const u32x4 (&pk)[QB][2], const u32x4 (&vf)[2][DB], int stage) {
-    const lds_char* base = lds + (stage < 0 ? 0 : stage) * R::kStageBytes;
+  // O^T += V^T P^T of a step for every block (each V^T fragment used QB times)
+  auto pv = [&](const u32x4 (&pk)[QB][2], const u32x4 (&vf)[2][DB]) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        u32x4 v = vf[s2][db];
-        if (stage >= 0) {
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(base + la.v[db][0] + s2 * 16 * R::kRowBytes));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(base + la.v[db][1] + s2 * 16 * R::kRowBytes));
-          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-          v = u32x4{l2[0], l2[1], h2[0], h2[1]};
-        }
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int b = 0; b < QB; ++b) blk[b].o[db] = mfma32(v, pk[b][s2], blk[b].o[db]);
-      }
+        for (int b = 0; b < QB; ++b) blk[b].o[db] = mfma32(vf[s2][db], pk[b][s2], blk[b].o[db]);
   };
 
   const int r0 = (n - 1) % G;
@@ -359,11 +350,12 @@ __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D
       }
       if (i + kAhead < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    if (!kEarlyV) read_v(vf, stage);
     if (j + NS - 1 < n) issue(j + NS - 1, (stage + NS - 1) % NS);
     // raised wave priority over the PV product: the SIMD's other wave, which is then
     // most likely in its softmax, yields issue slots to these MFMAs
     __builtin_amdgcn_s_setprio(1);
-    pv(pk, vf, kEarlyV ? -1 : stage);
+    pv(pk, vf);
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -390,7 +382,8 @@ __device__ __forceinline__ void run_steps(int n, lds_char* lds, const LaneAddr<D
   if (kEarlyV) read_v(vf, 0);
   u32x4 pk[QB][2];
   soft(s0, pk, true);
-  pv(pk, vf, kEarlyV ? -1 : 0);
+  if (!kEarlyV) read_v(vf, 0);
+  pv(pk, vf);
 }
 
 }  // namespace hc
