@@ -17,8 +17,9 @@
 // changes only with the chunk and the reference max. With frame parts, each of n_parts
 // workgroups walks its share of the frames and stores an fp32 partial that the merge
 // kernel joins. In final mode the result is merged with the dense current-block partial
-// by its log-sum-exp and written as bf16; in partial mode (classifier, frame parts) it
-// is stored as fp32; with cells the whole key set is walked here.
+// by its log-sum-exp and written as bf16; in partial mode (classifier, frame parts, tiles
+// run in the dense launch) it is stored as fp32; with cells the whole key set is walked
+// here.
 #pragma once
 #include "hc_pipe.h"
 

@@ -236,8 +236,8 @@ int32_t hc_decide(double cos_sink, double cos_dummy, double cos_spatial, double 
  * runs [8][16][2] = {first item, items} (-1 / 0 past n_runs[x]), n_runs [8], and the
  * longest queue; workgroup i runs on XCD i % 8, taking position i / 8 of its queue.
  * With the Spatial tiles in the launch, items from the dense item count on (see
- * hc_debug_routed_plan) are the tiles, Spatial head by head in head order within the
- * SpatialEntry list, tile_r x tile_c position tiles each.
+ * hc_debug_routed_plan) are the tiles: Spatial head by head in increasing head order,
+ * each head's tile_r x tile_c position tiles row-major (frame part by frame part).
  * hc_debug_spatial_plan: the Spatial launch of a routed call, host [5] = {tile rows,
  * tile columns, frame parts, partial slots of the whole call, 1 if the Spatial tiles
  * run as the last items of the dense launch}; zeros without Spatial heads (the slot
