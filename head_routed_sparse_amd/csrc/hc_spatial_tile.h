@@ -133,6 +133,11 @@ __device__ __forceinline__ void spatial_tile(const SpatialGeom& p, const Spatial
     u32x4 q[1][KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) q[0][ks] = *(const u32x4*)(qp + ks * 16 + half * 8);
+    // wait for the query loads here: the compiler does not count the ring's direct
+    // loads, and with these loads still pending it would wait at every step's score
+    // MFMAs for a vector-memory count that the direct loads then also have to reach,
+    // draining the ring's prefetch each step
+    wait_vmcnt<0>();
 
     // loads: step t = chunk t / n_frames of the union in frame f0 + t % n_frames, issued
     // in order
