@@ -295,6 +295,9 @@ void plan_splits_search(std::vector<Entry>& es, int nqt, int slot_budget, int n_
   }
 }
 
+// Planner decisions kept per input, at most this many at a time.
+constexpr size_t kMemoCap = 1024;
+
 void plan_splits(std::vector<Entry>& es, int nqt, int slot_budget, int n_slots, int64_t piece_bytes) {
   // decisions are kept per input (layers of one geometry and head mix plan alike)
   static std::mutex mu;
@@ -316,6 +319,7 @@ void plan_splits(std::vector<Entry>& es, int nqt, int slot_budget, int n_slots, 
   std::vector<std::pair<int, int>> val;
   for (const Entry& e : es) val.push_back({e.nsplit, e.split_len});
   std::lock_guard<std::mutex> lk(mu);
+  if (memo.size() >= kMemoCap) memo.clear();   // bounded in a long-lived process
   memo[key] = val;
 }
 
@@ -382,6 +386,7 @@ void choose_spatial_tile(int fh, int fw, int gh, int gw, bool cells, int n_heads
       }
     }
   std::lock_guard<std::mutex> lk(mu);
+  if (memo.size() >= kMemoCap) memo.clear();
   memo[key] = {*tile_r, *tile_c};
 }
 
