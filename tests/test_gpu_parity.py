@@ -101,6 +101,21 @@ def test_spatial_tiles_on_odd_frames(frame, variant):
           assert_close(got, want, *TOL["bf16"], what=f"{frame} v{variant} tile {tile_r}x{tile_c} parts {parts}"))
 
 
+@pytest.mark.parametrize("n_sp", [16, 17])
+def test_spatial_heads_at_the_fused_launch_limit(n_sp):
+    """At most 16 Spatial heads run their tiles in the dense launch: 16 with d = 128 are
+    fused, 17 take their own launch; both match the oracle."""
+    g = hin.Geometry(n_sp + 2, 128, 6, 9, 2, 8, 3, 3, "bf16")
+    labels = (P_,) * n_sp + (G_, S_)
+    inp = hin.generate(g, labels, seed=300 + n_sp)
+    t = to_device(inp)
+    buf = hc.hc_build_head_buffers(hc.make_desc(g), inp.labels, t["k_hist"], t["v_hist"], inp.n_hist_frames)
+    fused = hc.hc_debug_spatial_plan(buf)[4]
+    assert fused == (n_sp <= 16)
+    got = host(hc.hc_routed_attention(buf, t["q"], t["k_cur"], t["v_cur"]))
+    print(n_sp, fused, assert_close(got, orc.routed_attention(inp), *TOL["bf16"], what=f"{n_sp} Spatial heads"))
+
+
 def test_binding_rejects_bad_tensors():
     """Wrong dtype, too few elements or a strided view: refused before the library runs."""
     g = hin.Geometry(4, 64, 8, 8, 1, 5, 3, 3, "bf16")

@@ -236,6 +236,22 @@ def test_routed_workspace_fits_every_fill_state(name, variant):
         assert len(sizes) == 1, (name, variant, lab, sizes)
 
 
+def test_fused_launch_form_limits():
+    """The Spatial tiles join the dense launch for bf16, d = 128, sliding windows and at
+    most 16 Spatial heads with at least one stored history frame; otherwise they keep
+    their own launch (or have no history part at all)."""
+    def fused(g, labels, nb, variant=0):
+        return hc.hc_debug_spatial_plan(hc.hc_plan_head_buffers(hc.make_desc(g, variant), np.array(labels, np.int32), nb))[4]
+    g = hin.Geometry(18, 128, 6, 9, 2, 8, 3, 3, "bf16")
+    assert fused(g, [2] * 16 + [3, 0], 3) == 1
+    assert fused(g, [2] * 17 + [3], 3) == 0
+    assert fused(g, [2] * 16 + [3, 0], 0) == 0          # no history frame stored yet
+    assert fused(g, [2] * 16 + [3, 0], 3, variant=4) == 0
+    assert fused(g, [2] * 16 + [3, 0], 3, variant=2) == 0   # cells walk the current block too
+    assert fused(dataclasses.replace(g, head_dim=64), [2] * 16 + [3, 0], 3) == 0
+    assert fused(dataclasses.replace(g, dtype="f32"), [2] * 16 + [3, 0], 3) == 0
+
+
 @pytest.mark.parametrize("name,variant,want", [("720p", 0, (5, 6, 1, 1)), ("480p", 0, (5, 6, 1, 1)),
                                                ("1080p", 0, (4, 8, 1, 1)), ("720p", 2, (5, 5, 1, 0)),
                                                ("480p", 2, (5, 5, 2, 0)), ("480p", 4, (5, 6, 3, 0)),
