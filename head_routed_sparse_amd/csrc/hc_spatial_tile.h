@@ -140,28 +140,58 @@ __device__ __forceinline__ void spatial_tile(const SpatialGeom& p, const Spatial
     wait_vmcnt<0>();
 
     // loads: step t = chunk t / n_frames of the union in frame f0 + t % n_frames, issued
-    // in order
+    // in order. With the tables, the byte offsets of this lane's rows within a history
+    // frame are worked out once per chunk and the frame base advances one frame per
+    // step; larger unions (no tables) work each step's offsets out from the tokens,
+    // which keeps their register count.
     int iu = 0, ifr = 0;
-    int tok[R::kLoads];
+    auto row_tok = [&](int i) {   // token of this lane's row i of the current chunk
+      const int row = iu * kStep + la.ld_row[i];
+      return TABLE ? *(const __attribute__((address_space(3))) int*)(tok_tbl + 4 * row) : union_tok(row);
+    };
+    uint32_t off_h[R::kLoads];                 // (tables) row byte offsets within a history frame
+    int tok[R::kLoads];                        // (no tables) row tokens of the current chunk
+    const int64_t frame_h = (int64_t)S * hs;   // bytes per history frame
+    int64_t fb = 0;                            // (tables) byte offset of history frame f0 + ifr
     auto issue = [&](int, int stage) {
-      if (ifr == 0) {   // a new chunk: the tokens of this lane's rows
+      const int fr = f0 + ifr;
+      if constexpr (TABLE) {
+        if (ifr == 0) {   // a new chunk: the rows of this lane, from the part's first frame
+#pragma unroll
+          for (int i = 0; i < R::kLoads; ++i) off_h[i] = (uint32_t)(row_tok(i) * hs) + la.ld_chunk[i];
+          fb = (int64_t)f0 * frame_h;
+        }
+        if (!cells || fr < nh) {   // a history frame (sliding windows walk only these)
+#pragma unroll
+          for (int i = 0; i < R::kLoads; ++i) {
+            dma16(kh + fb, off_h[i], la.dst(lds, stage, wave, i, 0));
+            dma16(vh + fb, off_h[i], la.dst(lds, stage, wave, i, 1));
+          }
+          fb += frame_h;
+        } else {   // a current-block frame (cells): token stride
+          const int64_t cb = (int64_t)(fr - nh) * S * ts;
+#pragma unroll
+          for (int i = 0; i < R::kLoads; ++i) {
+            const uint32_t off = (uint32_t)(row_tok(i) * ts) + la.ld_chunk[i];
+            dma16(kcb + cb, off, la.dst(lds, stage, wave, i, 0));
+            dma16(vcb + cb, off, la.dst(lds, stage, wave, i, 1));
+          }
+        }
+      } else {
+        if (ifr == 0)
+#pragma unroll
+          for (int i = 0; i < R::kLoads; ++i) tok[i] = row_tok(i);
+        const bool cur = fr >= nh;
+        const int64_t stride = cur ? ts : hs;
+        const int64_t fbase = (int64_t)(cur ? fr - nh : fr) * S * stride;
+        const char* kb = (cur ? kcb : kh) + fbase;
+        const char* vb = (cur ? vcb : vh) + fbase;
 #pragma unroll
         for (int i = 0; i < R::kLoads; ++i) {
-          const int row = iu * kStep + la.ld_row[i];
-          tok[i] = TABLE ? *(const __attribute__((address_space(3))) int*)(tok_tbl + 4 * row) : union_tok(row);
+          const uint32_t off = (uint32_t)(tok[i] * stride) + la.ld_chunk[i];
+          dma16(kb, off, la.dst(lds, stage, wave, i, 0));
+          dma16(vb, off, la.dst(lds, stage, wave, i, 1));
         }
-      }
-      const int fr = f0 + ifr;
-      const bool cur = fr >= nh;
-      const int64_t stride = cur ? ts : hs;
-      const int64_t fbase = (int64_t)(cur ? fr - nh : fr) * S * stride;
-      const char* kb = (cur ? kcb : kh) + fbase;
-      const char* vb = (cur ? vcb : vh) + fbase;
-#pragma unroll
-      for (int i = 0; i < R::kLoads; ++i) {
-        const uint32_t off = (uint32_t)(tok[i] * stride) + la.ld_chunk[i];
-        dma16(kb, off, la.dst(lds, stage, wave, i, 0));
-        dma16(vb, off, la.dst(lds, stage, wave, i, 1));
       }
       if (++ifr == n_frames) {
         ifr = 0;
