@@ -32,6 +32,35 @@ __device__ __forceinline__ f32x4 mix_slots(const float* po, const float* pml, in
   return acc * (1.0f / L);
 }
 
+// The same mix for at most N slots, with every load issued before the first use (one
+// memory round trip instead of one for the maxima and one for the rest).
+template <int N>
+__device__ __forceinline__ f32x4 mix_few_slots(const float* po, const float* pml, int64_t lq, int D,
+                                               int slot, int n, int q, int d) {
+  float m[N], l[N];
+  f32x4 v[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {   // slots past n load the last slot again, with weight 0
+    const int64_t row = (slot + min(i, n - 1)) * lq + q;
+    const float2 ml = *(const float2*)(pml + row * 2);
+    m[i] = i < n ? ml.x : -INFINITY;
+    l[i] = ml.y;
+    v[i] = *(const f32x4*)(po + row * D + d);
+  }
+  float M = m[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) M = fmaxf(M, m[i]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float w = m[i] == -INFINITY ? 0.f : fast_exp2(m[i] - M);
+    L += w * l[i];
+    acc += w * v[i];
+  }
+  return acc * (1.0f / L);
+}
+
 template <bool kBf16>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   const MergeEntry e = p.e[blockIdx.y];
@@ -40,7 +69,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   const int q = blockIdx.x * (256 / tpq) + threadIdx.x / tpq;
   const int d = (threadIdx.x % tpq) * 4;
   if (q >= p.lq) return;
-  const f32x4 o = mix_slots(p.part_o, p.part_ml, p.lq, D, e.slot, e.nslot, q, d, nullptr);
+  const f32x4 o = e.nslot <= 4   ? mix_few_slots<4>(p.part_o, p.part_ml, p.lq, D, e.slot, e.nslot, q, d)
+                 : e.nslot <= 8  ? mix_few_slots<8>(p.part_o, p.part_ml, p.lq, D, e.slot, e.nslot, q, d)
+                 : e.nslot <= 16 ? mix_few_slots<16>(p.part_o, p.part_ml, p.lq, D, e.slot, e.nslot, q, d)
+                                 : mix_slots(p.part_o, p.part_ml, p.lq, D, e.slot, e.nslot, q, d, nullptr);
   const int64_t off = (int64_t)q * p.tok_stride + (int64_t)e.head * D + d;
   if (kBf16) {
     u32x2 w = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
