@@ -101,6 +101,24 @@ def test_spatial_tiles_on_odd_frames(frame, variant):
           assert_close(got, want, *TOL["bf16"], what=f"{frame} v{variant} tile {tile_r}x{tile_c} parts {parts}"))
 
 
+@pytest.mark.parametrize("variant,d", [(0, 128), (4, 128), (0, 64)])
+def test_spatial_unions_past_the_lds_tables(variant, d):
+    """16 x 16 windows: a tile's union spans more than the eight 32-key chunks the LDS
+    tables hold, so each chunk's tokens and window bits are worked out when it starts
+    (tiles in the dense launch, in their own launch, and d = 64)."""
+    g = hin.Geometry(3, d, 24, 30, 2, 8, 16, 16, "bf16")
+    inp = hin.generate(g, (P_, G_, P_), seed=500 + variant + d)
+    t = to_device(inp)
+    buf = hc.hc_build_head_buffers(hc.make_desc(g, variant), inp.labels, t["k_hist"], t["v_hist"],
+                                   inp.n_hist_frames)
+    tr, tc, parts, _, fused = hc.hc_debug_spatial_plan(buf)
+    assert fused == (variant == 0 and d == 128)
+    assert -(-min(tr + 15, g.frame_h) * min(tc + 15, g.frame_w) // 32) > 8   # an interior tile's union
+    got = host(hc.hc_routed_attention(buf, t["q"], t["k_cur"], t["v_cur"]))
+    print(variant, d, (tr, tc, parts),
+          assert_close(got, orc.routed_attention(inp), *TOL["bf16"], what=f"v{variant} d{d} tile {tr}x{tc}"))
+
+
 @pytest.mark.parametrize("n_sp", [16, 17])
 def test_spatial_heads_at_the_fused_launch_limit(n_sp):
     """At most 16 Spatial heads run their tiles in the dense launch: 16 with d = 128 are
