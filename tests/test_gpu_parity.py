@@ -119,6 +119,21 @@ def test_spatial_unions_past_the_lds_tables(variant, d):
           assert_close(got, orc.routed_attention(inp), *TOL["bf16"], what=f"v{variant} d{d} tile {tr}x{tc}"))
 
 
+@pytest.mark.parametrize("geom", [hin.Geometry(2, 128, 8, 8, 1, 40, 3, 3, "bf16"),
+                                  hin.Geometry(1, 128, 8, 8, 1, 64, 3, 3, "bf16"),
+                                  hin.Geometry(2, 64, 6, 8, 1, 48, 3, 3, "bf16")])
+def test_many_key_splits_merge(geom):
+    """Few queries against a long window: each Global head's keys are cut into 9 to 16
+    pieces (the merge's widest fast path) and joined again."""
+    inp = hin.generate(geom, (G_,) * geom.num_heads, seed=600 + geom.window_frames)
+    t = to_device(inp)
+    buf = hc.hc_build_head_buffers(hc.make_desc(geom), inp.labels, t["k_hist"], t["v_hist"], inp.n_hist_frames)
+    ents, _ = hc.hc_debug_routed_plan(buf)
+    assert all(9 <= int(e[3]) <= 16 for e in ents), [int(e[3]) for e in ents]
+    got = host(hc.hc_routed_attention(buf, t["q"], t["k_cur"], t["v_cur"]))
+    print([int(e[3]) for e in ents], assert_close(got, orc.routed_attention(inp), *TOL["bf16"], what=str(geom)))
+
+
 @pytest.mark.parametrize("n_sp", [16, 17])
 def test_spatial_heads_at_the_fused_launch_limit(n_sp):
     """At most 16 Spatial heads run their tiles in the dense launch: 16 with d = 128 are
