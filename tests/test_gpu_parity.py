@@ -523,10 +523,11 @@ def test_variant_rollout_dummy_buffer(dtype):
         hc.hc_append_chunk(buf, dev(k, dtype), dev(v, dtype))
 
 
-def test_variant_full_size_720p_sampled_rows():
-    """The pages' deployed paths at 720P: 10 x 10 cells for the Spatial heads and the
-    previous block for the Dummy heads."""
-    inp = hin.config_inputs("720p")
+@pytest.mark.parametrize("name", ["720p", "1080p"])
+def test_variant_full_size_sampled_rows(name):
+    """The pages' deployed paths at the benchmark's 720P and 1080P sizes: 10 x 10 cells
+    for the Spatial heads and the previous block for the Dummy heads."""
+    inp = hin.config_inputs(name)
     g = dataclasses.replace(inp.geom, grid_h=10, grid_w=10)
     inp = dataclasses.replace(inp, geom=g)
     t = to_device(inp)
@@ -534,4 +535,4 @@ def test_variant_full_size_720p_sampled_rows():
     out = host(hc.hc_routed_attention(buf, t["q"], t["k_cur"], t["v_cur"]))
     rows = sample_rows(g, n_random=96, seed=2)
     want = orc.routed_attention(inp, rows=rows, variant=3)
-    print(assert_close(out[rows], want, *TOL["bf16"], what="720p deployed variants"))
+    print(assert_close(out[rows], want, *TOL["bf16"], what=f"{name} deployed variants"))
