@@ -33,6 +33,15 @@ import numpy as np
 SINK, DUMMY, SPATIAL, GLOBAL = 0, 1, 2, 3
 COS_EPS = 1e-8
 
+
+
+def attention_scale(head_dim):
+    """Score scale of the attention the paths compute: 1/sqrt(d), scaled dot-product
+    attention with no bias (HeadCast Sec. 3.1). Owned here, not taken from the caller's
+    layer description, so that the oracle does not share it with the library's caller."""
+    return 1.0 / np.sqrt(float(head_dim))
+
+
 # Path variants the pages also describe (deployed forms; see key_set_mask):
 DUMMY_PREVIOUS_BLOCK = 1   # Dummy heads also see the latest finished block
 SPATIAL_CELLS = 2          # Spatial heads see their own non-overlapping cell in every frame
@@ -164,7 +173,7 @@ def path_attention(inp, h, cls, rows=None, block=512, grid=None, sink_proxy=Fals
     for b in range(0, rows.size, block):
         r = rows[b:b + block]
         m = key_set_mask(cls, g, inp.n_hist_frames, r, grid, sink_proxy, sink_proxy_includes_current, variant)
-        out[b:b + block], _ = masked_attention(qh[r], kh, vh, m, g.softmax_scale)
+        out[b:b + block], _ = masked_attention(qh[r], kh, vh, m, attention_scale(g.head_dim))
     return out
 
 
@@ -217,7 +226,7 @@ def brute_force_attention(inp, h, cls, t, grid=None, sink_proxy=False, variant=0
                 else:
                     tok = f * S + r * fw + c
                     kv, vv = inp.k_hist[tok, h, :], inp.v_hist[tok, h, :]
-                scores.append(float(np.dot(qv, kv.astype(np.float64))) * g.softmax_scale)
+                scores.append(float(np.dot(qv, kv.astype(np.float64))) * attention_scale(g.head_dim))
                 values.append(vv.astype(np.float64))
     mx = max(scores)
     w = [np.exp(s - mx) for s in scores]

@@ -63,7 +63,7 @@ def test_p2_softmax_rows_sum_to_one_and_vanish_outside_key_set(cls):
     rows = np.arange(geom.lq)
     qh, kh, vh = orc.head_window(inp.q, inp.k_hist, inp.v_hist, inp.k_cur, inp.v_cur, 0)
     m = orc.key_set_mask(cls, geom, inp.n_hist_frames, rows)
-    _, _, p = orc.masked_attention(qh, kh, vh, m, geom.softmax_scale, return_weights=True)
+    _, _, p = orc.masked_attention(qh, kh, vh, m, orc.attention_scale(geom.head_dim), return_weights=True)
     assert np.max(np.abs(p.sum(axis=1) - 1.0)) < 1e-12
     assert np.all(p[~m] == 0.0)
     assert np.all(p[m] > 0.0)
