@@ -462,3 +462,53 @@ def test_dense_xcd_queues_cover_items_balanced_longest_first(name, global_only):
     for gid, xs in spans.items():
         if n_groups[cost[gid]] >= 8:
             assert len(xs) <= 3, (gid, xs)
+
+
+def test_random_layers_plan_invariants():
+    """Seeded random layers (head count, head size, frame, block, window, grid, dtype,
+    variant and launch option, label mix, fill state of the window): every head planned
+    once, every key range cut into pieces that cover it exactly, every item of the dense
+    launch (Spatial tiles included when they join it) in exactly one XCD queue, the
+    partial slots within the workspace the handle asks for, and the launch form of the
+    Spatial path as its rules say."""
+    rng = np.random.default_rng(2024)
+    for case in range(600):
+        d = int(rng.choice([64, 128]))
+        C = int(rng.integers(1, 5))
+        g = hin.Geometry(int(rng.integers(1, 65)), d, int(rng.integers(1, 48)), int(rng.integers(1, 72)), C,
+                         C * int(rng.integers(1, 9)), int(rng.integers(1, 13)), int(rng.integers(1, 13)),
+                         str(rng.choice(["bf16", "f32"])))
+        variant = int(rng.integers(0, 8))
+        labels = rng.integers(0, 4, g.num_heads).astype(np.int32)
+        R = max(g.window_frames // C - 2, 0)
+        next_block = int(rng.integers(0, 2 * R + 4))
+        pb = hc.hc_plan_head_buffers(hc.make_desc(g, variant), labels, next_block)
+        what = (case, g, variant, list(labels), next_block)
+        ents, n_items = hc.hc_debug_routed_plan(pb)
+        heads = [int(e[0]) for e in ents]
+        assert len(set(heads)) == len(heads) and set(heads) <= set(range(g.num_heads)), what
+        qtile = int(ents[0, 7]) if len(ents) else 128
+        nqt = -(-g.lq // qtile)
+        begin = 0
+        for head, hist, cur, nsplit, split_len, slot, item_begin, _q in ents:
+            total = int(hist) + int(cur)
+            assert 0 <= hist <= (g.window_frames - C) * g.tokens_per_frame and total >= 1, what
+            assert nsplit >= 1 and split_len % 64 == 0, what
+            assert (nsplit - 1) * split_len < total <= nsplit * split_len, what
+            assert item_begin == begin, what
+            begin += int(nsplit) * nqt
+        assert begin == n_items, what
+        tr, tc, parts, slots, fused = hc.hc_debug_spatial_plan(pb)
+        n_sp = int(np.sum(labels == 2))
+        has_hist = len(orc.window_history_blocks(next_block, g.window_frames, C)) > 0
+        want_fused = (g.dtype == "bf16" and d == 128 and not variant & 6 and 0 < n_sp <= 16 and has_hist)
+        assert bool(fused) == want_fused, what
+        if n_items:
+            queues, _ = hc.hc_debug_dense_queues(pb)
+            n_all = n_items + (n_sp * -(-g.frame_h // tr) * -(-g.frame_w // tc) * parts if fused else 0)
+            seen = np.zeros(n_all, np.int64)
+            for q in queues:
+                for f, c in q:
+                    seen[f:f + c] += 1
+            assert np.all(seen == 1), what
+        assert hc.hc_routed_workspace_bytes(pb) >= slots * g.lq * (g.head_dim + 2) * 4, what
