@@ -134,6 +134,29 @@ def test_many_key_splits_merge(geom):
     print([int(e[3]) for e in ents], assert_close(got, orc.routed_attention(inp), *TOL["bf16"], what=str(geom)))
 
 
+def test_random_layers_match_oracle():
+    """Seeded random small layers (head count and size, frame, block, window and its
+    fill, grid, dtype, path variants and launch option, label mix) against the oracle on
+    every query row."""
+    rng = np.random.default_rng(77)
+    for case in range(16):
+        d = int(rng.choice([64, 128]))
+        C = int(rng.integers(1, 4))
+        g = hin.Geometry(int(rng.integers(1, 9)), d, int(rng.integers(1, 13)), int(rng.integers(1, 21)), C,
+                         C * int(rng.integers(1, 6)), int(rng.integers(1, 9)), int(rng.integers(1, 9)),
+                         str(rng.choice(["bf16", "bf16", "f32"])))
+        variant = int(rng.integers(0, 8))
+        labels = rng.integers(0, 4, g.num_heads).astype(np.int32)
+        n_hist = C * int(rng.integers(0, g.hist_frames // C + 1))
+        inp = hin.generate(g, labels, seed=900 + case, n_hist_frames=n_hist)
+        t = to_device(inp)
+        buf = hc.hc_build_head_buffers(hc.make_desc(g, variant), inp.labels, t["k_hist"], t["v_hist"], n_hist)
+        got = host(hc.hc_routed_attention(buf, t["q"], t["k_cur"], t["v_cur"]))
+        want = orc.routed_attention(inp, variant=variant & 3)
+        print(case, g, variant, list(labels), n_hist,
+              assert_close(got, want, *TOL[g.dtype], what=f"case {case}: {g} v{variant} {list(labels)} n_hist {n_hist}"))
+
+
 @pytest.mark.parametrize("n_sp", [16, 17])
 def test_spatial_heads_at_the_fused_launch_limit(n_sp):
     """At most 16 Spatial heads run their tiles in the dense launch: 16 with d = 128 are
