@@ -464,6 +464,42 @@ def test_classify_unplanted_statistics_match_oracle():
         assert np.allclose(stats[h], ref, atol=3e-3), (h, stats[h], ref)
 
 
+def test_classify_random_layers_match_oracle():
+    """Seeded random small layers, planted and not (head count and size, frame, block,
+    window and its fill, grid, dtype, gamma, proxy grid): the six statistics of every head
+    within 3e-3 of the oracle's, and the labels equal wherever every statistic is at
+    least 0.01 from its threshold (nearer, fp32 cosines and fp64 ones may fall on either
+    side)."""
+    rng = np.random.default_rng(55)
+    th = dict(orc.DEFAULT_PARAMS)
+    for case in range(12):
+        d = int(rng.choice([64, 128]))
+        C = int(rng.integers(1, 4))
+        g = hin.Geometry(int(rng.integers(1, 9)), d, int(rng.integers(2, 13)), int(rng.integers(2, 21)), C,
+                         C * int(rng.integers(2, 7)), int(rng.integers(1, 9)), int(rng.integers(1, 9)),
+                         str(rng.choice(["bf16", "bf16", "f32"])))
+        labels = rng.integers(0, 4, g.num_heads).astype(np.int32)
+        n_hist = C * int(rng.integers(1, g.hist_frames // C + 1))
+        inp = hin.generate(g, labels, seed=1100 + case, n_hist_frames=n_hist, planted=bool(case % 2))
+        params = dict(gamma=float(rng.choice([0.5, 5.0])))
+        gpu_params = dict(params)
+        if rng.integers(0, 2):
+            params["proxy_grid"] = (int(rng.integers(1, 9)), int(rng.integers(1, 9)))
+            gpu_params.update(proxy_grid_h=params["proxy_grid"][0], proxy_grid_w=params["proxy_grid"][1])
+        got, stats = classify_gpu(inp, **gpu_params)
+        want, ost = orc.classify_heads(inp, params)
+        what = (case, g, list(labels), n_hist, params)
+        for h in range(g.num_heads):
+            o = ost[h]
+            ref = [o["cos_sink"], o["cos_dummy"], o["cos_spatial"], o["p5"], o["mse"], o["score"]]
+            assert np.allclose(stats[h], ref, atol=3e-3), (what, h, stats[h], ref)
+            margins = [abs(o["cos_sink"] - th["theta_sink"]), abs(o["cos_dummy"] - th["theta_dummy"]),
+                       abs(o["cos_spatial"] - th["theta_spatial"]), abs(o["score"] - th["theta_score"])]
+            if min(margins) >= 0.01:
+                assert got[h] == want[h], (what, h, got[h], want[h], ref)
+        print(case, g, n_hist, params, list(want), list(got))
+
+
 @pytest.mark.parametrize("proxy", [(5, 5), (2, 7), (1, 1)])
 def test_classify_proxy_grid_statistics_match_oracle(proxy):
     """A Spatial proxy window other than the routing grid (the pages' radius-2, 5 x 5
