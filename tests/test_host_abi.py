@@ -512,3 +512,19 @@ def test_random_layers_plan_invariants():
                     seen[f:f + c] += 1
             assert np.all(seen == 1), what
         assert hc.hc_routed_workspace_bytes(pb) >= slots * g.lq * (g.head_dim + 2) * 4, what
+
+
+def test_random_slot_tables_match_oracle():
+    """Seeded random windows, label mixes, Dummy variants and block counts (the ring
+    rolling over several times): the handle's slot table equals the oracle's."""
+    rng = np.random.default_rng(31)
+    for case in range(400):
+        C = int(rng.integers(1, 5))
+        F = C * int(rng.integers(1, 10))
+        g = hin.Geometry(int(rng.integers(1, 17)), int(rng.choice([64, 128])), 3, 4, C, F, 2, 2, "bf16")
+        labels = rng.integers(0, 4, g.num_heads).astype(np.int32)
+        variant = int(rng.choice([0, 1]))
+        n = int(rng.integers(0, 4 * max(F // C, 1) + 3))
+        pb = hc.hc_plan_head_buffers(hc.make_desc(g, variant), labels, n)
+        want = orc.slot_table(labels, F, C, n, variant=orc.DUMMY_PREVIOUS_BLOCK if variant else 0)
+        assert np.array_equal(hc.hc_debug_slot_table(pb), want), (case, F, C, list(labels), variant, n)
