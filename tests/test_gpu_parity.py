@@ -365,6 +365,42 @@ def test_rollout_routed_matches_oracle_window(dtype):
         hc.hc_append_chunk(buf, dev(k, dtype), dev(v, dtype))
 
 
+def test_random_rollouts_match_oracle():
+    """Seeded random layers driven from an empty cache through the ring rolling over
+    (head count and size, frame, block, window, grid, dtype, Dummy variant, launch
+    option, label mix): after every append, the slot table equals the oracle's and the
+    routed output equals the oracle on the logical window."""
+    rng = np.random.default_rng(404)
+    for case in range(6):
+        d = int(rng.choice([64, 128]))
+        C = int(rng.integers(1, 4))
+        g = hin.Geometry(int(rng.integers(1, 7)), d, int(rng.integers(2, 9)), int(rng.integers(2, 13)), C,
+                         C * int(rng.integers(2, 6)), int(rng.integers(1, 6)), int(rng.integers(1, 6)),
+                         str(rng.choice(["bf16", "f32"])))
+        variant = int(rng.choice([0, 1, 4, 5]))
+        labels = rng.integers(0, 4, g.num_heads).astype(np.int32)
+        S, H = g.tokens_per_frame, g.num_heads
+        n_steps = g.window_frames // C + 3
+        blocks = [hin.round_to_bf16(rng.standard_normal((3, C * S, H, d), dtype=np.float32)) if g.dtype == "bf16"
+                  else rng.standard_normal((3, C * S, H, d), dtype=np.float32) for _ in range(n_steps)]
+        buf = hc.hc_build_head_buffers(hc.make_desc(g, variant), labels, None, None, 0)
+        ws = hc.routed_workspace(buf)
+        for step in range(n_steps):
+            q, k, v = blocks[step]
+            table = orc.slot_table(labels, g.window_frames, C, step,
+                                   variant=orc.DUMMY_PREVIOUS_BLOCK if variant & 1 else 0)
+            assert np.array_equal(hc.hc_debug_slot_table(buf), table), (case, step)
+            out = host(hc.hc_routed_attention(buf, dev(q, g.dtype), dev(k, g.dtype), dev(v, g.dtype), workspace=ws))
+            hist = orc.window_history_blocks(step, g.window_frames, C)
+            kh = np.concatenate([blocks[b][1] for b in hist]) if hist else np.zeros((0, H, d), np.float32)
+            vh = np.concatenate([blocks[b][2] for b in hist]) if hist else np.zeros((0, H, d), np.float32)
+            inp = hin.LayerInputs(g, labels, q, kh, vh, k, v, len(hist) * C)
+            assert_close(out, orc.routed_attention(inp, variant=variant & 3), *TOL[g.dtype],
+                         what=f"case {case} {g} v{variant} {list(labels)} step {step}")
+            hc.hc_append_chunk(buf, dev(k, g.dtype), dev(v, g.dtype))
+        print(case, g, variant, list(labels), n_steps)
+
+
 @pytest.mark.parametrize("name", ["480p", "720p", "1080p"])
 def test_full_size_sampled_rows(name):
     """The benchmark's workloads at full size; sampled query rows against the oracle, the
